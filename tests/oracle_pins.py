@@ -1,0 +1,447 @@
+"""Pins of the CPU oracle: each ``pin_*`` raises AssertionError when the oracle disagrees
+with something the pages or the mathematics fix independently of the oracle itself --
+values printed on the pages (tests/golden), closed forms, exact integer identities,
+brute force with scalar Python loops on tiny inputs, and library routines (torch CPU,
+float64) for the special cases that reduce to them.
+
+The module is imported by test_oracle_pins.py (which runs every pin) and by
+test_oracle_mutations.py (which plants mistakes in the oracle and checks that some pin
+catches each of them).
+"""
+from __future__ import annotations
+
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+import torch.nn.functional as TF
+
+import oracle.tp_oracle as O
+from workloads.configs import tensor_bytes
+
+GOLDEN = Path(__file__).parent / "golden"
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _ints(rng, shape, lo, hi) -> np.ndarray:
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float64)
+
+
+def brute_matmul(A, B) -> np.ndarray:
+    """Scalar triple loop (tiny inputs only)."""
+    A = np.asarray(A, dtype=np.float64).tolist()
+    B = np.asarray(B, dtype=np.float64).tolist()
+    n, k, m = len(A), len(B), len(B[0])
+    out = [[0.0] * m for _ in range(n)]
+    for i in range(n):
+        Ai = A[i]
+        for j in range(m):
+            s = 0.0
+            for t in range(k):
+                s += Ai[t] * B[t][j]
+            out[i][j] = s
+    return np.array(out)
+
+
+def _close(a, b, rtol, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    scale = max(1.0, float(np.max(np.abs(b)))) if b.size else 1.0
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= rtol * scale, f"{what}: max err {err:.3e} > {rtol:.1e} * {scale:.3e}"
+
+
+def _t(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+
+
+# ----------------------------------------------------------------------------- sharding
+def pin_shard_golden():
+    for line in (GOLDEN / "shard_examples.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        n, world, rank, start, stop = map(int, line.split())
+        assert O.shard_range(n, world, rank) == (start, stop), line
+        assert O.head_range(n, world, rank) == (start, stop), line
+
+
+def pin_shard_rejects():
+    for args in [(10, 4, 0), (4097, 2, 1), (8, 0, 0), (8, 2, 2), (8, 2, -1)]:
+        try:
+            O.shard_range(*args)
+        except ValueError:
+            continue
+        raise AssertionError(f"shard_range{args} did not reject")
+
+
+def pin_shard_tiles_exactly():
+    for n, world in [(12, 3), (48, 8), (4096, 4)]:
+        seen = []
+        for r in range(world):
+            a, b = O.shard_range(n, world, r)
+            assert b - a == n // world
+            seen.extend(range(a, b))
+        assert seen == list(range(n))
+
+
+# ----------------------------------------------------------------------------- linears
+def pin_column_concat_bruteforce():
+    rng = _rng(11)
+    X = rng.standard_normal((3, 5))
+    W = rng.standard_normal((5, 8))
+    ref = brute_matmul(X, W)
+    for world in (1, 2, 4, 8):
+        Y = O.concat_columns([O.col_linear(X, W, r, world) for r in range(world)])
+        _close(Y, ref, 1e-14, f"column concat world={world}")
+
+
+def pin_column_concat_integer_exact():
+    rng = _rng(12)
+    X = _ints(rng, (9, 24), -1, 1)
+    W = _ints(rng, (24, 32), -2, 2)
+    ref = brute_matmul(X, W)
+    for world in (2, 4):
+        blocks = [O.col_linear(X, W, r, world) for r in range(world)]
+        for r, b in enumerate(blocks):
+            c = 32 // world
+            assert np.array_equal(b, ref[:, r * c:(r + 1) * c]), f"block {r} of {world}"
+        assert np.array_equal(O.concat_columns(blocks), ref)
+
+
+def pin_row_partials_integer_exact():
+    rng = _rng(13)
+    X = _ints(rng, (7, 32), -1, 1)
+    W = _ints(rng, (32, 12), -2, 2)
+    ref = brute_matmul(X, W)
+    for world in (1, 2, 4, 8):
+        c = 32 // world
+        parts = [O.row_linear_partial(X, W, r, world) for r in range(world)]
+        for r, p in enumerate(parts):
+            assert np.array_equal(p, brute_matmul(X[:, r * c:(r + 1) * c], W[r * c:(r + 1) * c])), \
+                f"partial {r} of {world}"
+        assert np.array_equal(O.reduce_partials(parts), ref)
+        assert np.array_equal(O.reduce_partials(parts[::-1]), ref)
+
+
+def pin_row_partials_float():
+    rng = _rng(14)
+    X = rng.standard_normal((4, 6))
+    W = rng.standard_normal((6, 3))
+    parts = [O.row_linear_partial(X, W, r, 3) for r in range(3)]
+    _close(O.reduce_partials(parts), brute_matmul(X, W), 1e-14, "row sum")
+
+
+def pin_rows_subset():
+    rng = _rng(15)
+    X = rng.standard_normal((10, 8))
+    W = rng.standard_normal((8, 6))
+    rows = [9, 0, 4]
+    _close(O.col_linear(X, W, 1, 2, "gelu_tanh", rows),
+           O.col_linear(X, W, 1, 2, "gelu_tanh")[rows], 0, "col rows")
+    _close(O.row_linear_partial(X, W, 1, 2, rows), O.row_linear_partial(X, W, 1, 2)[rows],
+           0, "row rows")
+
+
+def pin_power_of_two_scaling_exact():
+    rng = _rng(16)
+    X = rng.standard_normal((5, 16))
+    W = rng.standard_normal((16, 8))
+    for r in range(2):
+        assert np.array_equal(O.col_linear(4.0 * X, W, r, 2), 4.0 * O.col_linear(X, W, r, 2))
+        assert np.array_equal(O.row_linear_partial(X, 0.5 * W, r, 2),
+                              0.5 * O.row_linear_partial(X, W, r, 2))
+
+
+def pin_inner_dim_checked():
+    try:
+        O.col_linear(np.zeros((2, 3)), np.zeros((4, 4)), 0, 2)
+    except ValueError:
+        return
+    raise AssertionError("mismatched inner dimension accepted")
+
+
+# ----------------------------------------------------------------------------- GeLU
+def pin_gelu_closed_forms():
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    x = np.linspace(-8, 8, 161)
+    g = O.gelu_tanh(x)
+    # g(x) - g(-x) = x exactly in the mathematics (tanh is odd).
+    assert np.max(np.abs((g - O.gelu_tanh(-x)) - x)) < 1e-13
+    assert abs(O.gelu_tanh(np.array([30.0]))[0] - 30.0) < 1e-12
+    assert abs(O.gelu_tanh(np.array([-30.0]))[0]) < 1e-12
+
+
+def pin_gelu_library():
+    x = np.linspace(-10, 10, 2001)
+    ref = TF.gelu(_t(x), approximate="tanh").numpy()
+    _close(O.gelu_tanh(x), ref, 1e-14, "gelu vs torch tanh-GeLU")
+
+
+def pin_gelu_approximates_erf_form():
+    x = np.linspace(-6, 6, 1201)
+    erf_form = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in x])
+    d = np.abs(O.gelu_tanh(x) - erf_form)
+    assert d.max() < 1e-3, "not an approximation of GeLU"
+    assert d.max() > 1e-6, "erf form instead of the tanh form"
+
+
+def pin_column_gelu_library():
+    rng = _rng(17)
+    X = rng.standard_normal((4, 8))
+    W = rng.standard_normal((8, 6))
+    ref = TF.gelu(_t(brute_matmul(X, W)), approximate="tanh").numpy()
+    Y = O.concat_columns([O.col_linear(X, W, r, 3, "gelu_tanh") for r in range(3)])
+    _close(Y, ref, 1e-13, "column + GeLU")
+
+
+# ----------------------------------------------------------------------------- LayerNorm
+def pin_layer_norm_library():
+    rng = _rng(18)
+    h = 3.0 * rng.standard_normal((6, 33)) + 1.5
+    g = 1 + 0.5 * rng.standard_normal(33)
+    b = 0.5 * rng.standard_normal(33)
+    ref = TF.layer_norm(_t(h), (33,), _t(g), _t(b), eps=1e-5).numpy()
+    _close(O.layer_norm(h, g, b, 1e-5), ref, 1e-13, "layer_norm vs torch")
+
+
+def pin_layer_norm_closed_forms():
+    rng = _rng(19)
+    b = rng.standard_normal(16)
+    y = O.layer_norm(np.full((2, 16), 3.25), np.ones(16), b, 1e-5)
+    _close(y, np.broadcast_to(b, (2, 16)), 1e-15, "constant row maps to beta")
+    # biased variance: row [0, 2] has mean 1 and variance 1, so eps=0 gives [-1, 1]
+    y = O.layer_norm(np.array([[0.0, 2.0]]), eps=0.0)
+    _close(y, [[-1.0, 1.0]], 1e-15, "two-element row")
+    h = 2.0 * rng.standard_normal((4, 64)) + 0.3
+    y = O.layer_norm(h, eps=1e-2)
+    var = h.var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) < 1e-13
+    _close((y * y).mean(axis=1), var / (var + 1e-2), 1e-13, "mean square")
+
+
+def pin_reduce_residual_layernorm():
+    rng = _rng(20)
+    parts = [_ints(rng, (3, 8), -5, 5) for _ in range(4)]
+    R = _ints(rng, (3, 8), -3, 3)
+    h, y = O.reduce_residual_layernorm(parts, R)
+    assert y is None
+    assert np.array_equal(h, R + parts[0] + parts[1] + parts[2] + parts[3])
+    g = rng.standard_normal(8)
+    b = rng.standard_normal(8)
+    h, y = O.reduce_residual_layernorm(parts, R, g, b, 1e-5)
+    ref = TF.layer_norm(_t(h), (8,), _t(g), _t(b), eps=1e-5).numpy()
+    _close(y, ref, 1e-13, "fused LN")
+    h0, y0 = O.reduce_residual_layernorm([], R, g, b, 1e-5)
+    assert np.array_equal(h0, R)
+    _close(y0, TF.layer_norm(_t(R), (8,), _t(g), _t(b), eps=1e-5).numpy(), 1e-13, "plain LN")
+
+
+# ----------------------------------------------------------------------------- attention
+def _attn_inputs(seed, batch, seq, H, scale=0.7):
+    rng = _rng(seed)
+    Xn = rng.standard_normal((batch * seq, H))
+    Wqkv = scale * rng.standard_normal((H, 3 * H)) / math.sqrt(H) * 2.0
+    Wo = rng.standard_normal((H, H)) / math.sqrt(H)
+    return Xn, Wqkv, Wo
+
+
+def pin_attention_library_sdpa():
+    batch, seq, nh, d = 2, 7, 4, 4
+    H = nh * d
+    Xn, Wqkv, _ = _attn_inputs(21, batch, seq, H)
+    for causal in (True, False):
+        A = O.attention_heads(Xn, Wqkv, nh, d, 0, 1, batch, seq, causal)
+        x = _t(Xn).reshape(batch, seq, H)
+        W = _t(Wqkv)
+        q = (x @ W[:, :H]).reshape(batch, seq, nh, d).transpose(1, 2)
+        k = (x @ W[:, H:2 * H]).reshape(batch, seq, nh, d).transpose(1, 2)
+        v = (x @ W[:, 2 * H:]).reshape(batch, seq, nh, d).transpose(1, 2)
+        o = TF.scaled_dot_product_attention(q, k, v, is_causal=causal)
+        ref = o.transpose(1, 2).reshape(batch * seq, H).numpy()
+        _close(A, ref, 1e-12, f"attention vs SDPA causal={causal}")
+
+
+def pin_attention_prefix_mean():
+    batch, seq, nh, d = 2, 6, 2, 4
+    H = nh * d
+    Xn, Wqkv, _ = _attn_inputs(22, batch, seq, H)
+    Wqkv = Wqkv.copy()
+    Wqkv[:, :H] = 0.0  # zero queries: all scores 0, uniform weights over visible keys
+    V = brute_matmul(Xn, Wqkv[:, 2 * H:])
+    for causal in (True, False):
+        A = O.attention_heads(Xn, Wqkv, nh, d, 0, 1, batch, seq, causal)
+        ref = np.zeros_like(V)
+        for b in range(batch):
+            for i in range(seq):
+                hi = i + 1 if causal else seq
+                ref[b * seq + i] = V[b * seq: b * seq + hi].sum(axis=0) / hi
+        _close(A, ref, 1e-14, f"prefix mean causal={causal}")
+
+
+def pin_attention_first_query():
+    batch, seq, nh, d = 3, 5, 2, 4
+    H = nh * d
+    Xn, Wqkv, _ = _attn_inputs(23, batch, seq, H, scale=3.0)
+    A = O.attention_heads(Xn, Wqkv, nh, d, 0, 1, batch, seq, True)
+    V = brute_matmul(Xn, Wqkv[:, 2 * H:])
+    for b in range(batch):
+        _close(A[b * seq], V[b * seq], 1e-14, "first query sees only itself")
+
+
+def pin_attention_bruteforce():
+    batch, seq, nh, d, world = 2, 3, 2, 2, 2
+    H = nh * d
+    Xn, Wqkv, Wo = _attn_inputs(24, batch, seq, H, scale=2.0)
+    Q = brute_matmul(Xn, Wqkv[:, :H])
+    K = brute_matmul(Xn, Wqkv[:, H:2 * H])
+    V = brute_matmul(Xn, Wqkv[:, 2 * H:])
+    for r in range(world):
+        A = O.attention_heads(Xn, Wqkv, nh, d, r, world, batch, seq, True)
+        Z = O.attn_head_shard(Xn, Wqkv, Wo, nh, d, r, world, batch, seq, True)
+        hl = nh // world
+        ref = np.zeros((batch * seq, hl * d))
+        for b in range(batch):
+            for i in range(seq):
+                for jh in range(hl):
+                    h = r * hl + jh
+                    cs = range(h * d, (h + 1) * d)
+                    sc = [sum(Q[b * seq + i][c] * K[b * seq + j][c] for c in cs) / math.sqrt(d)
+                          for j in range(i + 1)]
+                    m = max(sc)
+                    w = [math.exp(s - m) for s in sc]
+                    tot = sum(w)
+                    for c_i, c in enumerate(cs):
+                        ref[b * seq + i][jh * d + c_i] = sum(
+                            w[j] * V[b * seq + j][c] for j in range(i + 1)) / tot
+        _close(A, ref, 1e-13, f"attention brute force rank {r}")
+        _close(Z, brute_matmul(ref, Wo[r * hl * d:(r + 1) * hl * d]), 1e-13, f"O partial rank {r}")
+
+
+def _torch_mha(Xn, Wqkv, Wo, nh, batch, seq, causal):
+    """Full multi-head attention with output projection (torch, float64)."""
+    H = Xn.shape[1]
+    x = _t(Xn).reshape(batch, seq, H).transpose(0, 1)  # [seq, batch, H]
+    W = _t(Wqkv)
+    mask = None
+    if causal:
+        mask = torch.triu(torch.ones(seq, seq, dtype=torch.bool), diagonal=1)
+    out, _ = TF.multi_head_attention_forward(
+        x, x, x, H, nh, None, None, None, None, False, 0.0,
+        _t(Wo).T.contiguous(), None, training=False, need_weights=False, attn_mask=mask,
+        use_separate_proj_weight=True, q_proj_weight=W[:, :H].T.contiguous(),
+        k_proj_weight=W[:, H:2 * H].T.contiguous(), v_proj_weight=W[:, 2 * H:].T.contiguous())
+    return out.transpose(0, 1).reshape(batch * seq, H).numpy()
+
+
+def pin_attention_head_split_equals_mha():
+    batch, seq, nh, d = 2, 9, 8, 4
+    H = nh * d
+    Xn, Wqkv, Wo = _attn_inputs(25, batch, seq, H)
+    for causal in (True, False):
+        ref = _torch_mha(Xn, Wqkv, Wo, nh, batch, seq, causal)
+        for world in (1, 2, 4, 8):
+            parts = [O.attn_head_shard(Xn, Wqkv, Wo, nh, d, r, world, batch, seq, causal)
+                     for r in range(world)]
+            _close(O.reduce_partials(parts), ref, 1e-12, f"head split world={world}")
+
+
+def pin_attention_rows_subset():
+    batch, seq, nh, d = 2, 11, 4, 4
+    H = nh * d
+    Xn, Wqkv, Wo = _attn_inputs(26, batch, seq, H)
+    rows = [21, 0, 5, 11, 12, 10]
+    for causal in (True, False):
+        full = O.attn_head_shard(Xn, Wqkv, Wo, nh, d, 1, 2, batch, seq, causal)
+        sub = O.attn_head_shard(Xn, Wqkv, Wo, nh, d, 1, 2, batch, seq, causal, rows)
+        _close(sub, full[rows], 1e-14, "row subset")
+
+
+# ----------------------------------------------------------------------------- MLP, block
+def pin_mlp_bruteforce():
+    rng = _rng(27)
+    X = rng.standard_normal((3, 4))
+    A = rng.standard_normal((4, 8)) / 2
+    B = rng.standard_normal((8, 4)) / 2
+    g = TF.gelu(_t(brute_matmul(X, A)), approximate="tanh").numpy()
+    ref = brute_matmul(g, B)
+    for world in (1, 2, 4):
+        Z = O.reduce_partials([O.mlp_shard(X, A, B, r, world) for r in range(world)])
+        _close(Z, ref, 1e-13, f"MLP world={world}")
+
+
+def pin_mlp_equals_single_card():
+    rng = _rng(28)
+    X = rng.standard_normal((16, 32))
+    A = rng.standard_normal((32, 128)) / math.sqrt(32)
+    B = rng.standard_normal((128, 32)) / math.sqrt(128)
+    ref = (TF.gelu(_t(X) @ _t(A), approximate="tanh") @ _t(B)).numpy()
+    for world in (2, 4, 8):
+        Z = O.reduce_partials([O.mlp_shard(X, A, B, r, world) for r in range(world)])
+        _close(Z, ref, 1e-13, f"MLP single card world={world}")
+
+
+def _block_inputs(seed, batch, seq, nh, d, F):
+    rng = _rng(seed)
+    H = nh * d
+    X = rng.standard_normal((batch * seq, H))
+    Wqkv = rng.standard_normal((H, 3 * H)) / math.sqrt(H)
+    Wo = rng.standard_normal((H, H)) / math.sqrt(H)
+    W1 = rng.standard_normal((H, F)) / math.sqrt(H)
+    W2 = rng.standard_normal((F, H)) / math.sqrt(F)
+    g1, b1, g2, b2 = (1 + 0.3 * rng.standard_normal(H), 0.3 * rng.standard_normal(H),
+                      1 + 0.3 * rng.standard_normal(H), 0.3 * rng.standard_normal(H))
+    return X, Wqkv, Wo, W1, W2, g1, b1, g2, b2
+
+
+def _torch_block(X, Wqkv, Wo, W1, W2, g1, b1, g2, b2, nh, batch, seq, causal, eps=1e-5):
+    H = X.shape[1]
+    xn = TF.layer_norm(_t(X), (H,), _t(g1), _t(b1), eps=eps).numpy()
+    h = _t(X) + _t(_torch_mha(xn, Wqkv, Wo, nh, batch, seq, causal))
+    hn = TF.layer_norm(h, (H,), _t(g2), _t(b2), eps=eps)
+    return (h + TF.gelu(hn @ _t(W1), approximate="tanh") @ _t(W2)).numpy()
+
+
+def pin_block_equals_single_card():
+    batch, seq, nh, d, F = 2, 6, 4, 4, 64
+    args = _block_inputs(29, batch, seq, nh, d, F)
+    ref = _torch_block(*args, nh, batch, seq, True)
+    _close(O.block_forward(*args, n_heads=nh, head_dim=d, batch=batch, seq=seq), ref, 1e-12,
+           "single-device block")
+    for world in (1, 2, 4):
+        res = O.block_shard(*args, n_heads=nh, head_dim=d, world=world, batch=batch, seq=seq)
+        _close(res["out"], ref, 1e-12, f"block shard world={world}")
+
+
+def pin_block_rows_subset():
+    batch, seq, nh, d, F = 2, 7, 4, 4, 32
+    args = _block_inputs(30, batch, seq, nh, d, F)
+    full = O.block_shard(*args, n_heads=nh, head_dim=d, world=2, batch=batch, seq=seq)
+    rows = [13, 3, 7, 0]
+    sub = O.block_shard(*args, n_heads=nh, head_dim=d, world=2, batch=batch, seq=seq, rows=rows)
+    for key in ("h", "hn", "out"):
+        _close(sub[key], full[key][rows], 1e-14, key)
+    for r in range(2):
+        _close(sub["attn_parts"][r], full["attn_parts"][r][rows], 1e-14, "attn part")
+
+
+# ----------------------------------------------------------------------------- accounting
+def pin_byte_accounting_golden():
+    vals = {}
+    for line in (GOLDEN / "byte_accounting.txt").read_text().splitlines():
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            vals[k] = int(v)
+    one = tensor_bytes(2048, 4096, "bf16")
+    assert one == vals["tensor_SH_bf16"]
+    assert 2 * one == vals["allreduce_SH_bf16_page_count"]
+    assert 4 * one == vals["block_two_allreduces"]
+
+
+ALL_PINS = {name: fn for name, fn in sorted(globals().items())
+            if name.startswith("pin_") and callable(fn)}
