@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the tensor-parallel Transformer-block shard on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: the block
+workload H=12288, 96 heads x 128, F=49152, 8 simulated tensor-parallel ranks (12 heads and
+an FFN slice of 6144 each), batch 4 x seq 2048, causal, bf16 with fp32 accumulation:
+
+    xn = LN(X)                                   reduce kernel, no partials
+    for r in 0..7: attention-head shard of r     QKV GEMM, attention, O GEMM -> fp32 partial
+    h, hn = X + sum_r partials, LN(h)            reduce + residual + LayerNorm
+    for r in 0..7: MLP shard of r                column GEMM + GeLU, row GEMM -> fp32 partial
+    out = h + sum_r partials                     reduce + residual
+
+Inputs are generated and resident in HBM before the timed region.  `value` is the whole
+step's algorithmic flops (all 8 ranks' shards) divided by the measured step time, in
+TFLOP/s.  Per-kernel durations come from HIP events recorded on the launch stream inside
+the timed region; the roofline object reports the dominant GEMM (the column-parallel
+GEMM + GeLU of the MLP).  The CPU baseline times the float64 oracle on a bounded row
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import generate, get_config  # noqa: E402
+from workloads.configs import rank_flops, reduce_bytes  # noqa: E402
+
+WORKLOAD = "block_bf16_tp8"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, t, qkv_vals) -> dict:
+    """The oracle as it stands, on a bounded row sample of the same block workload."""
+    import oracle.tp_oracle as O
+    S = cfg.seq
+    rows = np.unique(np.concatenate([np.linspace(0, S - 1, 24).astype(np.int64), [S - 1]]))
+    g, b = t["gamma"].values(), t["beta"].values()
+    args = (t["X"].values(), qkv_vals, t["Wo"].values(), t["W1"].values(), t["W2"].values(),
+            g, b, g, b)
+    t0 = time.perf_counter()
+    O.block_shard(*args, n_heads=cfg.n_heads, head_dim=cfg.head_dim, world=cfg.world,
+                  batch=cfg.batch, seq=S, causal=True, eps=cfg.eps, rows=rows,
+                  keep_partials=False)
+    dt = time.perf_counter() - t0
+    # algorithmic flops the sample needs: K and V over the causal prefix of every rank,
+    # Q, attention and O for the sampled rows, and the MLP of every rank for those rows.
+    H, P, d = cfg.hidden, cfg.world, cfg.head_dim
+    hl = cfg.n_heads // P
+    nb = hl * d
+    prefix = int(rows.max()) + 1
+    R = len(rows)
+    per_rank = (2.0 * prefix * H * 2 * nb + 2.0 * R * H * nb
+                + sum(4.0 * d * (int(i) + 1) * hl for i in rows) + 2.0 * R * nb * H
+                + 2.0 * 2.0 * R * H * (cfg.ffn // P))
+    flops = per_rank * P
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": (f"float64 oracle of the whole 8-rank block for {R} query rows of sequence 0 "
+                       f"(positions 0..{prefix - 1}, keys/values over the full causal prefix): "
+                       f"{flops / 1e9:.0f} GFLOP in {dt:.1f} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the tensor-parallel ranks are simulated in turn "
+              "on that GPU, and no multi-GPU path exists in this library.", file=sys.stderr)
+        return 2
+
+    import torch
+    from megatron_tensor_transformer_linear_amd import pipeline as pl
+    from megatron_tensor_transformer_linear_amd import tp
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    cfg = get_config(WORKLOAD)
+    t0 = time.time()
+    t = generate(cfg)
+    qkv_bits = np.ascontiguousarray(np.hstack([t["Wq"].data, t["Wk"].data, t["Wv"].data]))
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+
+    def up(a):
+        return pl.to_device(a, "bf16", dev)
+
+    blk = pl.BlockShard(up(t["X"].data), up(qkv_bits), up(t["Wo"].data), up(t["W1"].data),
+                        up(t["W2"].data), up(t["gamma"].data), up(t["beta"].data),
+                        up(t["gamma"].data), up(t["beta"].data), cfg.world, cfg.batch, cfg.seq,
+                        cfg.n_heads, cfg.head_dim, True, cfg.eps)
+    torch.cuda.synchronize()
+    log("inputs resident in HBM")
+
+    stream = torch.cuda.current_stream()
+    ev = {k: [] for k in ("pre_ln", "attn", "reduce1", "mlp_col", "mlp_row", "reduce2")}
+
+    def timed(key, fn, record):
+        if record:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            ev[key].append((s, e))
+        else:
+            fn()
+
+    def step(record: bool):
+        timed("pre_ln", blk.pre_ln, record)
+        for r in range(cfg.world):
+            timed("attn", lambda r=r: blk.attn(r), record)
+        timed("reduce1", blk.reduce1, record)
+        for r in range(cfg.world):
+            timed("mlp_col", lambda r=r: blk.mlp_col(r), record)
+            timed("mlp_row", lambda r=r: blk.mlp_row(r), record)
+        timed("reduce2", blk.reduce2, record)
+
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"{args.steps} timed steps in {elapsed:.3f} s")
+
+    def avg_ms(key):
+        return float(np.mean([s.elapsed_time(e) for s, e in ev[key]]))
+
+    fl = rank_flops(cfg)
+    step_flops = cfg.world * sum(fl.values())
+    value = step_flops * args.steps / elapsed / 1e12
+    ms_step = elapsed / args.steps * 1e3
+
+    col_ms = avg_ms("mlp_col")
+    col_flops = fl["mlp_col"]
+    achieved = col_flops / (col_ms * 1e-3) / 1e12
+    T, H = cfg.tokens, cfg.hidden
+    r1_bytes = reduce_bytes(T, H, cfg.world, "bf16", residual=True, h_out=True, y_out=True)
+    r2_bytes = reduce_bytes(T, H, cfg.world, "bf16", residual=True, h_out=True, y_out=False)
+    ln_bytes = reduce_bytes(T, H, 0, "bf16", residual=True, h_out=False, y_out=True)
+    stages = {}
+    for key in ev:
+        ms = avg_ms(key)
+        entry = {"avg_ms": round(ms, 4), "launches_per_step": len(ev[key]) // args.steps}
+        if key == "attn":
+            entry["tflops"] = round((fl["qkv"] + fl["attn_core"] + fl["o_proj"]) / ms / 1e9, 1)
+        elif key in ("mlp_col", "mlp_row"):
+            entry["tflops"] = round(fl[key] / ms / 1e9, 1)
+        elif key in ("reduce1", "reduce2", "pre_ln"):
+            nbytes = {"reduce1": r1_bytes, "reduce2": r2_bytes, "pre_ln": ln_bytes}[key]
+            entry["gbs"] = round(nbytes / ms / 1e6, 1)
+            entry["hbm_frac"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)
+        stages[key] = entry
+
+    result = {
+        "metric": "TFLOP/s per TP-rank layer shard (MLP+attn) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("block_bf16_tp8: Transformer block shard, H=12288, 96 heads x 128, "
+                         "FFN 49152, 8 simulated TP ranks computed in turn, batch 4 x seq 2048, "
+                         "causal"),
+            "global_batch": cfg.batch, "seq_len": cfg.seq, "tp_ranks_simulated": cfg.world,
+            "parallelism": "tp8 simulated on 1 GPU",
+            "step_gflop": round(step_flops / 1e9, 1),
+            "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_bf16_kernel<EPI_GELU_TANH> (MLP column GEMM + GeLU, 8192x12288x6144)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": col_flops,
+            "avg_launch_ms": round(col_ms, 4),
+        },
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, t, np.hstack(
+            [t["Wq"].values(), t["Wk"].values(), t["Wv"].values()]))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

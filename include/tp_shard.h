@@ -1,0 +1,150 @@
+/* tp_shard.h -- C ABI of the MI355X (gfx950) tensor-parallel layer-shard library.
+ *
+ * One call computes one simulated tensor-parallel rank's shard of a Megatron-style
+ * Transformer layer on one GPU.  Where the layer's tensor-parallel form places an
+ * all-gather between GPUs, the caller concatenates the ranks' outputs in one HBM buffer
+ * (by pointing each rank's output at its column block); where it places an all-reduce,
+ * the ranks' fp32 partials are stacked in HBM and summed by
+ * tp_partial_reduce_residual_ln, fused with the residual add and LayerNorm.
+ *
+ * Sources (web pages on tensor parallelism):
+ *   typc.net "张量并行：千亿大模型突破单卡显存限制的底层技术", sections 2.1, 2.2, 3;
+ *   0539edu.com TP / 3D-parallelism tutorial, sections 1.1 and 1.2 (formulas 1.1-1.13);
+ *   pwwt.cn TP layout walk-through, sections 1.1-1.2 (figures 1-2), 2.1-2.3 (figures 3-5),
+ *   3.1-3.4 (the weight-chunk helper and the column/row parallel layers), 5.3 and 6.3.
+ *
+ * Conventions shared by every call
+ *   - A linear layer is Y = X.W with X [seq, H] and W [H, N] (pwwt.cn section 1.1); every
+ *     matrix is row-major.  Weights are stored [in, out].
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the caller.  The
+ *     library allocates nothing, frees nothing and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call is
+ *     asynchronous on that stream and never synchronises.
+ *   - Ranks are numbered 0..world-1; rank r owns block r of a split dimension, and rank 0
+ *     owns the first block (typc.net section 2.1; pwwt.cn section 3.1).
+ *   - Accumulation is always fp32.  bf16 results are rounded to nearest even.
+ *   - Every argument is validated BEFORE any HIP call.  On error the call returns a
+ *     negative tp_status, launches nothing and leaves every output untouched.  A launch
+ *     failure returns TP_ERR_LAUNCH.
+ *   - Alignment: pointers 16-byte aligned; leading dimensions, shard widths and the
+ *     column offsets they imply are multiples of 8 elements.
+ *   - Calls are re-entrant; concurrent calls on different streams may not write the same
+ *     output.  Results are deterministic (fixed summation order, no atomics).
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = -1,      /* a required pointer is NULL */
+  TP_ERR_SHAPE = -2,     /* a size is <= 0, a leading dimension is too small, or a size is unsupported */
+  TP_ERR_DIVISIBLE = -3, /* a split dimension is not a multiple of world */
+  TP_ERR_RANK = -4,      /* world < 1, or rank outside [0, world) */
+  TP_ERR_DTYPE = -5,     /* unknown dtype / activation, or a dtype the call does not support */
+  TP_ERR_ALIGN = -6,     /* pointer, leading dimension or shard offset misaligned */
+  TP_ERR_WORKSPACE = -7, /* workspace NULL or smaller than tp_attn_workspace_bytes */
+  TP_ERR_LAUNCH = -8     /* the HIP runtime reported an error at launch */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;         /* io dtype of X, W, Y, residual, LN */
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
+
+/* Column-parallel linear with fused activation (the all-gather form).
+ *
+ *   Y[t, j] = act( sum_k X[t, k] * W[k, rank*N/world + j] ),  t < seq, j < N/world
+ *
+ * X [seq, H] dense (ld H) is the full input every rank holds; W [H, N] dense (ld N) is the
+ * full weight, of which rank `rank` uses the column block [rank*N/world, (rank+1)*N/world)
+ * (typc.net section 2.1; 0539edu.com section 1.1 "column split", figure 1.2; pwwt.cn
+ * sections 1.1 and 3.2).  Y receives the N/world output columns with leading dimension
+ * ldy >= N/world.  To concatenate the simulated ranks' outputs (the all-gather) pass
+ * Y = Yfull + rank*N/world and ldy = N.  act is tp_act: GeLU with the tanh form
+ *   0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+ * is applied per element before rounding to the io dtype (0539edu.com section 1.2.1: the
+ * elementwise activation commutes with the column split).  dtype TP_BF16 or TP_F32.
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE (seq, H, N <= 0 or ldy < N/world), TP_ERR_DIVISIBLE
+ * (N % world), TP_ERR_RANK, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_LAUNCH. */
+int tp_col_linear_gelu(const void* X, const void* W, void* Y, int64_t ldy,
+                       int64_t seq, int64_t H, int64_t N, int rank, int world,
+                       int act, int dtype, void* stream);
+
+/* Row-parallel linear, partial sum of one rank (the all-reduce form, before the reduce).
+ *
+ *   Zpart[t, n] = sum_{k < K/world} X[t, rank*K/world + k] * W[rank*K/world + k, n]
+ *
+ * X [seq, K] with leading dimension ldx >= K is the full input; its column block `rank` is
+ * the rank's input shard (for the MLP this is exactly the column block the column-parallel
+ * call wrote, e.g. Yfull with ldx = K).  W [K, N] dense (ld N); rank `rank` uses its row
+ * block [rank*K/world, (rank+1)*K/world) (typc.net section 2.2; 0539edu.com section 1.1
+ * formula 1.1 "outer-product-sum split"; pwwt.cn sections 1.2 and 3.3).  Zpart [seq, N] is
+ * dense fp32 whatever the io dtype; the full result is the sum of all ranks' partials.
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE (ldx < K), TP_ERR_DIVISIBLE (K % world), TP_ERR_RANK,
+ * TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_LAUNCH. */
+int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpart,
+                          int64_t seq, int64_t K, int64_t N, int rank, int world,
+                          int dtype, void* stream);
+
+/* Workspace bytes tp_attn_head_shard needs for these sizes; 0 if the sizes are invalid. */
+size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_heads,
+                               int head_dim, int world, int dtype);
+
+/* Attention-head shard of one rank: column-split QKV projection, per-head softmax
+ * attention over the rank's heads, row-split output projection (0539edu.com section 1.2.2,
+ * formulas 1.8-1.13, figure 1.5; pwwt.cn section 2.2, figure 4; typc.net section 3).
+ *
+ *   heads of rank r: [r*n_heads/world, (r+1)*n_heads/world), hl = n_heads/world, d = head_dim
+ *   Q_r | K_r | V_r  = Xn . Wqkv[:, column blocks of those heads]          [T, 3*hl*d]
+ *   O_h = softmax(Q_h K_h^T / sqrt(d) + causal mask) V_h   per sequence and head
+ *   A_r = concat of O_h over the rank's heads, ascending                  [T, hl*d]
+ *   Zpart = A_r . Wo[r*hl*d : (r+1)*hl*d, :]                              [T, H] fp32
+ *
+ * Xn [batch*seq, H] dense: the (already normalised) input, sequences contiguous.  Wqkv
+ * [H, 3H] dense = [Wq | Wk | Wv], head h owning columns [h*d, (h+1)*d) of each block.  Wo
+ * [H, H] dense.  H must equal n_heads*head_dim; head_dim must be 128.  causal: key j is
+ * visible to query i iff j <= i within the same sequence.  Only dtype TP_BF16.
+ * workspace (device, >= tp_attn_workspace_bytes, 256-byte aligned) receives, as a
+ * documented by-product, QKV_r bf16 [T, 3*hl*d] at offset 0 and A_r bf16 [T, hl*d] right
+ * after it (offset T*3*hl*d*2 bytes).
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DIVISIBLE (n_heads % world), TP_ERR_RANK,
+ * TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_LAUNCH. */
+int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
+                       int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                       int rank, int world, int causal, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The all-reduce replacement, fused with the residual add and LayerNorm (pwwt.cn section
+ * 2.3: the single all-reduce sits just before the residual add, and fusing it with the
+ * residual add or the next LayerNorm's statistics; section 6.3: residual + LayerNorm as
+ * one fused op with a consistent statistics order).  Over `rows` rows of width H:
+ *
+ *   h = residual + sum_{p = 0}^{n_parts-1} parts[p * part_stride + ...]   fp32, p ascending
+ *   y = (h - mean(h)) / sqrt(var(h) + eps) * gamma + beta    biased var, fp32 statistics of h
+ *
+ * parts: n_parts dense fp32 [rows, H] blocks, block p starting at parts + p*part_stride
+ * (part_stride >= rows*H elements).  n_parts == 0 gives a plain LayerNorm of `residual`
+ * (parts may then be NULL).  residual may be NULL (treated as 0); h_out may be NULL;
+ * gamma == NULL skips the LayerNorm (y_out is then ignored); beta == NULL means 0.
+ * residual, gamma, beta, h_out and y_out use `dtype`; h_out and y_out must not alias the
+ * parts.  Requires H % 8 == 0 and H <= 65536.
+ * Errors: TP_ERR_NULL (no input at all, or gamma given with y_out NULL), TP_ERR_SHAPE,
+ * TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_LAUNCH. */
+int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_stride,
+                                  const void* residual, const void* gamma, const void* beta,
+                                  float eps, void* h_out, void* y_out,
+                                  int64_t rows, int64_t H, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a tp_status value. */
+const char* tp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

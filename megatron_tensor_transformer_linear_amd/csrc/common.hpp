@@ -1,0 +1,104 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// Epilogues of the GEMM tile.
+enum Epilogue : int {
+  EPI_STORE = 0,       // Y (io dtype) = acc
+  EPI_GELU_TANH = 1,   // Y (io dtype) = gelu_tanh(acc)
+  EPI_PARTIAL_F32 = 2  // Z (fp32) = acc
+};
+
+// C = epi(A . B) for one rank's shard.
+//   A [M, K] row-major, leading dimension lda, already offset to the rank's first column.
+//   B [K, *] row-major, leading dimension ldb, already offset to the rank's first row and
+//     first column.  Logical column n of B lives at physical column
+//       (n / b_blk) * b_blk_stride + (n % b_blk)
+//     which lets the QKV projection read three separated column blocks of [Wq | Wk | Wv]
+//     as one operand (b_blk = N gives the plain contiguous case).
+//   C [M, N] row-major, leading dimension ldc (bf16 / fp32 per dtype and epilogue).
+struct GemmDesc {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  int64_t b_blk;
+  int64_t b_blk_stride;
+  void* C;
+  int64_t ldc;
+  int64_t M, N, K;
+  int epi;
+};
+
+// Causal / full attention over one rank's heads.
+//   qkv [batch*seq, 3*hl*d] bf16 = [Q_r | K_r | V_r], head h at columns h*d of each block.
+//   out [batch*seq, hl*d] bf16, heads concatenated in ascending order.
+struct AttnDesc {
+  const bf16_t* qkv;
+  bf16_t* out;
+  int64_t batch, seq;
+  int hl, d;
+  int causal;
+  float scale_log2;  // log2(e) / sqrt(d)
+};
+
+// h = residual + sum_p parts[p]; y = LayerNorm(h) * gamma + beta.
+struct ReduceDesc {
+  const float* parts;
+  int n_parts;
+  int64_t part_stride;
+  const void* residual;
+  const void* gamma;
+  const void* beta;
+  float eps;
+  void* h_out;
+  void* y_out;
+  int64_t rows, H;
+  int bf16;  // io dtype is bf16 (else fp32)
+};
+
+hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t stream);
+hipError_t launch_attention(const AttnDesc& a, hipStream_t stream);
+hipError_t launch_reduce_ln(const ReduceDesc& r, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// GeLU, tanh form.  0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), so
+//   gelu(x) = x / (1 + exp(-2u)),  u = sqrt(2/pi) (x + 0.044715 x^3),
+// with exp evaluated as exp2 on the hardware transcendental unit.
+__device__ __forceinline__ float gelu_tanh_f32(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float m2log2e = -2.0f * 1.4426950408889634f;
+  float u = k0 * (x + k1 * x * x * x);
+  float e = __builtin_amdgcn_exp2f(m2log2e * u);
+  return x / (1.0f + e);
+}
+
+}  // namespace tpk

@@ -1,0 +1,104 @@
+// fp32 MFMA GEMM tile for gfx950 (io dtype fp32): the column / row-parallel linears of the
+// small fp32 MLP.  Same contract and epilogues as the bf16 tile (0539edu.com TP tutorial
+// section 1.1, formula 1.1 and figure 1.2), built on v_mfma_f32_16x16x4_f32.
+//
+// Tile 64 x 64 x 16, 256 threads = 4 waves in a 2 x 2 grid, each wave 32 x 32 as 2 x 2 blocks
+// of 16 x 16.  Operand layout of the 16x16x4 instruction: A lane l holds A[l % 16][l / 16],
+// B lane l holds B[l / 16][l % 16]; accumulator element r of lane l is C[4 (l / 16) + r][l % 16].
+// These fp32 shapes are a few MFLOP, so the tile is single-buffered and launch-bound.
+#include "common.hpp"
+
+namespace tpk {
+namespace {
+
+constexpr int TM = 64, TN = 64, TK = 16;
+constexpr int NT = 256;
+
+template <int EPI>
+__global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmDesc g) {
+  __shared__ float As[TM][TK + 1];
+  __shared__ __attribute__((aligned(16))) float Bs[TK][TN + 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t M = g.M, N = g.N, K = g.K;
+  const int64_t m0 = (int64_t)blockIdx.y * TM, n0 = (int64_t)blockIdx.x * TN;
+  const float* __restrict__ A = (const float*)g.A;
+  const float* __restrict__ B = (const float*)g.B;
+
+  // A tile: thread -> row tid/4, k chunk (tid%4)*4.  B tile: k-row tid/16, n chunk (tid%16)*4.
+  const int a_r = tid >> 2, a_k = (tid & 3) * 4;
+  const int b_r = tid >> 4, b_n = (tid & 15) * 4;
+  const int64_t b_nlog = n0 + b_n;
+  const bool b_nvalid = b_nlog < N;
+  const int64_t b_col = (b_nlog / g.b_blk) * g.b_blk_stride + (b_nlog % g.b_blk);
+
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t k0 = 0; k0 < K; k0 += TK) {
+    {
+      const int64_t row = m0 + a_r, k = k0 + a_k;
+      float4 v = (row < M && k < K) ? *(const float4*)(A + row * g.lda + k) : make_float4(0, 0, 0, 0);
+      As[a_r][a_k + 0] = v.x;
+      As[a_r][a_k + 1] = v.y;
+      As[a_r][a_k + 2] = v.z;
+      As[a_r][a_k + 3] = v.w;
+      const int64_t kb = k0 + b_r;
+      float4 w = (b_nvalid && kb < K) ? *(const float4*)(B + kb * g.ldb + b_col) : make_float4(0, 0, 0, 0);
+      *(float4*)&Bs[b_r][b_n] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 4) {
+      float a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = As[wm * 32 + i * 16 + (lane & 15)][kk + (lane >> 4)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = Bs[kk + (lane >> 4)][wn * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = n0 + wn * 32 + j * 16 + (lane & 15);
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
+        if (row >= M) continue;
+        float v = acc[i][j][r];
+        if (EPI == EPI_GELU_TANH) v = gelu_tanh_f32(v);
+        ((float*)g.C)[row * g.ldc + col] = v;
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t stream) {
+  const int64_t tm = (g.M + TM - 1) / TM, tn = (g.N + TN - 1) / TN;
+  if (tm <= 0 || tn <= 0) return hipSuccess;
+  if (tm > 65535 || tn > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)tn, (unsigned)tm), block(NT);
+  switch (g.epi) {
+    case EPI_STORE:
+    case EPI_PARTIAL_F32: hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, grid, block, 0, stream, g); break;
+    case EPI_GELU_TANH: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU_TANH>, grid, block, 0, stream, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpk

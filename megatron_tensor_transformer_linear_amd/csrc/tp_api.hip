@@ -1,0 +1,233 @@
+// C ABI of the tensor-parallel layer-shard library: argument validation, shard-offset
+// arithmetic (64-bit integers) and kernel launches.  Every check runs before the first HIP
+// call, so an invalid call launches nothing and leaves its outputs untouched.
+#include <math.h>
+
+#include "../../include/tp_shard.h"
+#include "common.hpp"
+
+using namespace tpk;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool mult8(int64_t v) { return (v & 7) == 0; }
+
+inline int check_rank(int rank, int world) {
+  if (world < 1 || rank < 0 || rank >= world) return TP_ERR_RANK;
+  return TP_OK;
+}
+
+inline int launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
+
+struct AttnSizes {
+  int64_t T, hl, nb, qkv_bytes, a_bytes, total;
+};
+
+int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim, int world,
+               AttnSizes* s) {
+  if (world < 1) return TP_ERR_RANK;
+  if (batch <= 0 || seq <= 0 || H <= 0 || n_heads <= 0 || head_dim <= 0) return TP_ERR_SHAPE;
+  if ((int64_t)n_heads * head_dim != H || head_dim != 128) return TP_ERR_SHAPE;
+  if (n_heads % world) return TP_ERR_DIVISIBLE;
+  s->T = batch * seq;
+  s->hl = n_heads / world;
+  s->nb = s->hl * head_dim;
+  s->qkv_bytes = s->T * 3 * s->nb * 2;
+  s->a_bytes = s->T * s->nb * 2;
+  s->total = ((s->qkv_bytes + s->a_bytes) + 255) & ~(int64_t)255;
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(int status) {
+  switch (status) {
+    case TP_OK: return "TP_OK: success";
+    case TP_ERR_NULL: return "TP_ERR_NULL: a required pointer is NULL";
+    case TP_ERR_SHAPE: return "TP_ERR_SHAPE: invalid or unsupported size or leading dimension";
+    case TP_ERR_DIVISIBLE: return "TP_ERR_DIVISIBLE: split dimension not divisible by world";
+    case TP_ERR_RANK: return "TP_ERR_RANK: world < 1 or rank outside [0, world)";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unknown or unsupported dtype or activation";
+    case TP_ERR_ALIGN: return "TP_ERR_ALIGN: misaligned pointer, leading dimension or shard offset";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_LAUNCH: return "TP_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown tp_status";
+  }
+}
+
+int tp_col_linear_gelu(const void* X, const void* W, void* Y, int64_t ldy, int64_t seq,
+                       int64_t H, int64_t N, int rank, int world, int act, int dtype,
+                       void* stream) {
+  if (!X || !W || !Y) return TP_ERR_NULL;
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  if (seq <= 0 || H <= 0 || N <= 0) return TP_ERR_SHAPE;
+  if (N % world) return TP_ERR_DIVISIBLE;
+  const int64_t nl = N / world;
+  if (ldy < nl) return TP_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return TP_ERR_ALIGN;
+  if (!mult8(H) || !mult8(N) || !mult8(nl) || !mult8(ldy)) return TP_ERR_ALIGN;
+
+  const size_t es = dtype == TP_BF16 ? 2 : 4;
+  GemmDesc g;
+  g.A = X;
+  g.lda = H;
+  g.B = (const char*)W + (size_t)rank * nl * es;  // column block `rank` of W[H, N]
+  g.ldb = N;
+  g.b_blk = nl;
+  g.b_blk_stride = 0;
+  g.C = Y;
+  g.ldc = ldy;
+  g.M = seq;
+  g.N = nl;
+  g.K = H;
+  g.epi = act == TP_ACT_GELU_TANH ? EPI_GELU_TANH : EPI_STORE;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  return launched(dtype == TP_BF16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s));
+}
+
+int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpart, int64_t seq,
+                          int64_t K, int64_t N, int rank, int world, int dtype, void* stream) {
+  if (!X || !W || !Zpart) return TP_ERR_NULL;
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  if (seq <= 0 || K <= 0 || N <= 0) return TP_ERR_SHAPE;
+  if (ldx < K) return TP_ERR_SHAPE;
+  if (K % world) return TP_ERR_DIVISIBLE;
+  const int64_t kl = K / world;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Zpart)) return TP_ERR_ALIGN;
+  if (!mult8(ldx) || !mult8(kl) || !mult8(N)) return TP_ERR_ALIGN;
+
+  const size_t es = dtype == TP_BF16 ? 2 : 4;
+  GemmDesc g;
+  g.A = (const char*)X + (size_t)rank * kl * es;       // column block `rank` of X[seq, K]
+  g.lda = ldx;
+  g.B = (const char*)W + (size_t)rank * kl * N * es;   // row block `rank` of W[K, N]
+  g.ldb = N;
+  g.b_blk = N;
+  g.b_blk_stride = 0;
+  g.C = Zpart;
+  g.ldc = N;
+  g.M = seq;
+  g.N = N;
+  g.K = kl;
+  g.epi = EPI_PARTIAL_F32;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  return launched(dtype == TP_BF16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s));
+}
+
+size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_heads,
+                               int head_dim, int world, int dtype) {
+  if (dtype != TP_BF16) return 0;
+  AttnSizes s;
+  if (attn_sizes(batch, seq, H, n_heads, head_dim, world, &s) != TP_OK) return 0;
+  return (size_t)s.total;
+}
+
+int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
+                       int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                       int rank, int world, int causal, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (!Xn || !Wqkv || !Wo || !Zpart) return TP_ERR_NULL;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  AttnSizes s;
+  if (int st = attn_sizes(batch, seq, H, n_heads, head_dim, world, &s)) return st;
+  if (!workspace || workspace_bytes < (size_t)s.total) return TP_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return TP_ERR_ALIGN;
+  if (!aligned16(Xn) || !aligned16(Wqkv) || !aligned16(Wo) || !aligned16(Zpart))
+    return TP_ERR_ALIGN;
+
+  bf16_t* ws_qkv = (bf16_t*)workspace;
+  bf16_t* ws_a = (bf16_t*)((char*)workspace + s.qkv_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  // Column-parallel QKV: logical column n of the rank's [Q_r | K_r | V_r] is physical column
+  // (n / nb) * H + rank * nb + n % nb of [Wq | Wk | Wv].
+  GemmDesc q;
+  q.A = Xn;
+  q.lda = H;
+  q.B = (const bf16_t*)Wqkv + (size_t)rank * s.nb;
+  q.ldb = 3 * H;
+  q.b_blk = s.nb;
+  q.b_blk_stride = H;
+  q.C = ws_qkv;
+  q.ldc = 3 * s.nb;
+  q.M = s.T;
+  q.N = 3 * s.nb;
+  q.K = H;
+  q.epi = EPI_STORE;
+  if (launch_gemm_bf16(q, st) != hipSuccess) return TP_ERR_LAUNCH;
+
+  AttnDesc a;
+  a.qkv = ws_qkv;
+  a.out = ws_a;
+  a.batch = batch;
+  a.seq = seq;
+  a.hl = (int)s.hl;
+  a.d = head_dim;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  if (launch_attention(a, st) != hipSuccess) return TP_ERR_LAUNCH;
+
+  // Row-parallel output projection over the rank's rows of Wo.
+  GemmDesc o;
+  o.A = ws_a;
+  o.lda = s.nb;
+  o.B = (const bf16_t*)Wo + (size_t)rank * s.nb * H;
+  o.ldb = H;
+  o.b_blk = H;
+  o.b_blk_stride = 0;
+  o.C = Zpart;
+  o.ldc = H;
+  o.M = s.T;
+  o.N = H;
+  o.K = s.nb;
+  o.epi = EPI_PARTIAL_F32;
+  return launched(launch_gemm_bf16(o, st));
+}
+
+int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_stride,
+                                  const void* residual, const void* gamma, const void* beta,
+                                  float eps, void* h_out, void* y_out, int64_t rows, int64_t H,
+                                  int dtype, void* stream) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (n_parts < 0) return TP_ERR_SHAPE;
+  if (n_parts > 0 && !parts) return TP_ERR_NULL;
+  if (n_parts == 0 && !residual) return TP_ERR_NULL;
+  if (gamma && !y_out) return TP_ERR_NULL;
+  if (!gamma && !h_out) return TP_ERR_NULL;
+  if (rows <= 0 || H <= 0 || H > 65536) return TP_ERR_SHAPE;
+  if (!(eps >= 0.0f) || isinf(eps)) return TP_ERR_SHAPE;
+  if (n_parts > 1 && part_stride < rows * H) return TP_ERR_SHAPE;
+  if (!mult8(H)) return TP_ERR_ALIGN;
+  if (n_parts > 1 && (part_stride & 3)) return TP_ERR_ALIGN;
+  const void* ptrs[] = {parts, residual, gamma, beta, h_out, y_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return TP_ERR_ALIGN;
+
+  ReduceDesc r;
+  r.parts = parts;
+  r.n_parts = n_parts;
+  r.part_stride = part_stride;
+  r.residual = residual;
+  r.gamma = gamma;
+  r.beta = beta;
+  r.eps = eps;
+  r.h_out = h_out;
+  r.y_out = gamma ? y_out : nullptr;
+  r.rows = rows;
+  r.H = H;
+  r.bf16 = dtype == TP_BF16;
+  (void)hipGetLastError();
+  return launched(launch_reduce_ln(r, (hipStream_t)stream));
+}
+
+}  // extern "C"

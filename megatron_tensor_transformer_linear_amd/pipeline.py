@@ -1,0 +1,247 @@
+"""The simulated tensor-parallel ranks composed from the library calls, on one GPU.
+
+Each class owns the device buffers of one workload and issues the C-ABI calls in the
+order the tensor-parallel layer runs them, one rank after another on one stream:
+
+  * the MLP (0539edu.com TP tutorial section 1.2.1; typc.net section 3): per rank, the
+    column-parallel linear with GeLU writes its block of the hidden activation into one
+    full-width buffer (the all-gather becomes a column offset), then the row-parallel
+    linear reads that same block and writes an fp32 partial; the partials are reduced in
+    HBM together with the residual add and LayerNorm;
+  * the attention-head shard (0539edu.com section 1.2.2; pwwt.cn section 2.2): per rank,
+    QKV column split, the rank's heads, O row split to an fp32 partial;
+  * the block (pwwt.cn section 2.1, figure 3): LayerNorm, attention shard of every rank,
+    reduce + residual + LayerNorm, MLP shard of every rank, reduce + residual.
+
+torch provides device memory and the stream only; all arithmetic is in the HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import tp
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def tp_dtype(dtype: str) -> int:
+    return tp.TP_BF16 if dtype == "bf16" else tp.TP_F32
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Copy a host array to the device: float32 values, or bf16 bit patterns (uint16 or
+    int16) reinterpreted as bfloat16."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+        return t.view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+class MLPShard:
+    """Column-parallel A (GeLU) then row-parallel B, P ranks, then the fused reduce.
+
+    residual_ln=True: h = X + sum_r Z_r and y = LN(h) (io dtype).  Otherwise the partials
+    are only summed, into Z (fp32)."""
+
+    def __init__(self, X, A, B, world: int, dtype: str, gamma=None, beta=None,
+                 eps: float = 1e-5, residual_ln: bool = True, stream=None):
+        self.X, self.A, self.B = X, A, B
+        self.T, self.H = X.shape
+        self.F = A.shape[1]
+        self.P = world
+        self.dt = tp_dtype(dtype)
+        self.gamma, self.beta, self.eps = gamma, beta, eps
+        self.residual_ln = residual_ln
+        self.stream = stream
+        dev = X.device
+        self.Yfull = torch.empty(self.T, self.F, dtype=torch_dtype(dtype), device=dev)
+        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        if residual_ln:
+            self.h = torch.empty(self.T, self.H, dtype=torch_dtype(dtype), device=dev)
+            self.y = torch.empty_like(self.h)
+        else:
+            self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
+
+    def column(self, r: int):
+        fl = self.F // self.P
+        tp.tp_col_linear_gelu(self.X, self.A, self.Yfull[:, r * fl:], self.F, self.T, self.H,
+                              self.F, r, self.P, tp.TP_ACT_GELU_TANH, self.dt, self.stream)
+
+    def row(self, r: int):
+        tp.tp_row_linear_partial(self.Yfull, self.F, self.B, self.parts[r], self.T, self.F,
+                                 self.H, r, self.P, self.dt, self.stream)
+
+    def reduce(self):
+        n = self.T * self.H
+        if self.residual_ln:
+            tp.tp_partial_reduce_residual_ln(self.parts, self.P, n, self.X, self.gamma, self.beta,
+                                             self.eps, self.h, self.y, self.T, self.H, self.dt,
+                                             self.stream)
+        else:
+            tp.tp_partial_reduce_residual_ln(self.parts, self.P, n, None, None, None, 0.0, self.Z,
+                                             None, self.T, self.H, tp.TP_F32, self.stream)
+
+    def step(self):
+        for r in range(self.P):
+            self.column(r)
+            self.row(r)
+        self.reduce()
+
+
+class LinearShard:
+    """One linear X[T,H].W[H,N]: the column block of chosen ranks, and the row split of
+    every rank with the fp32 partial sum Z."""
+
+    def __init__(self, X, W, world: int, dtype: str, col_ranks=(0,), stream=None):
+        self.X, self.W = X, W
+        self.T, self.H = X.shape
+        self.N = W.shape[1]
+        self.P = world
+        self.dt = tp_dtype(dtype)
+        self.col_ranks = tuple(col_ranks)
+        self.stream = stream
+        dev = X.device
+        nl = self.N // world
+        self.Ycol = {r: torch.empty(self.T, nl, dtype=torch_dtype(dtype), device=dev)
+                     for r in self.col_ranks}
+        self.parts = torch.empty(world, self.T, self.N, dtype=torch.float32, device=dev)
+        self.Z = torch.empty(self.T, self.N, dtype=torch.float32, device=dev)
+
+    def column(self, r: int, act: int = tp.TP_ACT_NONE):
+        Y = self.Ycol[r]
+        tp.tp_col_linear_gelu(self.X, self.W, Y, Y.stride(0), self.T, self.H, self.N, r, self.P,
+                              act, self.dt, self.stream)
+
+    def row(self, r: int):
+        tp.tp_row_linear_partial(self.X, self.H, self.W, self.parts[r], self.T, self.H, self.N, r,
+                                 self.P, self.dt, self.stream)
+
+    def reduce(self):
+        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.N, None, None, None,
+                                         0.0, self.Z, None, self.T, self.N, tp.TP_F32, self.stream)
+
+    def step(self):
+        for r in self.col_ranks:
+            self.column(r)
+        for r in range(self.P):
+            self.row(r)
+        self.reduce()
+
+
+class AttnShard:
+    """The attention-head shard of every rank, and the fp32 sum of their partials."""
+
+    def __init__(self, Xn, Wqkv, Wo, world: int, batch: int, seq: int, n_heads: int,
+                 head_dim: int, causal: bool = True, stream=None):
+        self.Xn, self.Wqkv, self.Wo = Xn, Wqkv, Wo
+        self.T, self.H = Xn.shape
+        self.P, self.batch, self.seq = world, batch, seq
+        self.nh, self.d, self.causal = n_heads, head_dim, causal
+        self.stream = stream
+        dev = Xn.device
+        self.ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, self.H, n_heads, head_dim, world,
+                                                   tp.TP_BF16)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid attention sizes")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
+
+    def workspace_views(self):
+        """(QKV_r [T, 3 nb], A_r [T, nb]) bf16 views of the workspace of the last rank run."""
+        nb = (self.nh // self.P) * self.d
+        n_qkv = self.T * 3 * nb
+        flat = self.ws.view(torch.bfloat16)
+        return flat[:n_qkv].view(self.T, 3 * nb), flat[n_qkv:n_qkv + self.T * nb].view(self.T, nb)
+
+    def rank(self, r: int, out: Optional[torch.Tensor] = None):
+        tp.tp_attn_head_shard(self.Xn, self.Wqkv, self.Wo, self.parts[r] if out is None else out,
+                              self.batch, self.seq, self.H, self.nh, self.d, r, self.P,
+                              int(self.causal), tp.TP_BF16, self.ws, self.ws_bytes, self.stream)
+
+    def reduce(self):
+        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, None, None, None,
+                                         0.0, self.Z, None, self.T, self.H, tp.TP_F32, self.stream)
+
+    def step(self):
+        for r in range(self.P):
+            self.rank(r)
+        self.reduce()
+
+
+class BlockShard:
+    """The whole Transformer block with every rank's attention and MLP shard:
+        xn = LN1(X); h = X + sum_r Attn_r(xn); hn = LN2(h); out = h + sum_r MLP_r(hn)."""
+
+    def __init__(self, X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, world: int,
+                 batch: int, seq: int, n_heads: int, head_dim: int, causal: bool = True,
+                 eps: float = 1e-5, stream=None):
+        self.X, self.Wqkv, self.Wo, self.W1, self.W2 = X, Wqkv, Wo, W1, W2
+        self.g1, self.b1, self.g2, self.b2 = gamma1, beta1, gamma2, beta2
+        self.T, self.H = X.shape
+        self.F = W1.shape[1]
+        self.P, self.batch, self.seq = world, batch, seq
+        self.nh, self.d, self.causal, self.eps = n_heads, head_dim, causal, eps
+        self.stream = stream
+        dev = X.device
+        bf = torch.bfloat16
+        self.xn = torch.empty(self.T, self.H, dtype=bf, device=dev)
+        self.h = torch.empty_like(self.xn)
+        self.hn = torch.empty_like(self.xn)
+        self.out = torch.empty_like(self.xn)
+        self.Yfull = torch.empty(self.T, self.F, dtype=bf, device=dev)
+        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        self.ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, self.H, n_heads, head_dim, world,
+                                                   tp.TP_BF16)
+        if self.ws_bytes == 0:
+            raise ValueError("invalid attention sizes")
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+
+    def pre_ln(self):
+        tp.tp_partial_reduce_residual_ln(None, 0, 0, self.X, self.g1, self.b1, self.eps, None,
+                                         self.xn, self.T, self.H, tp.TP_BF16, self.stream)
+
+    def attn(self, r: int):
+        tp.tp_attn_head_shard(self.xn, self.Wqkv, self.Wo, self.parts[r], self.batch, self.seq,
+                              self.H, self.nh, self.d, r, self.P, int(self.causal), tp.TP_BF16,
+                              self.ws, self.ws_bytes, self.stream)
+
+    def reduce1(self):
+        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.X, self.g2,
+                                         self.b2, self.eps, self.h, self.hn, self.T, self.H,
+                                         tp.TP_BF16, self.stream)
+
+    def mlp_col(self, r: int):
+        fl = self.F // self.P
+        tp.tp_col_linear_gelu(self.hn, self.W1, self.Yfull[:, r * fl:], self.F, self.T, self.H,
+                              self.F, r, self.P, tp.TP_ACT_GELU_TANH, tp.TP_BF16, self.stream)
+
+    def mlp_row(self, r: int):
+        tp.tp_row_linear_partial(self.Yfull, self.F, self.W2, self.parts[r], self.T, self.F,
+                                 self.H, r, self.P, tp.TP_BF16, self.stream)
+
+    def reduce2(self):
+        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.h, None, None,
+                                         0.0, self.out, None, self.T, self.H, tp.TP_BF16,
+                                         self.stream)
+
+    def attention_phase(self):
+        self.pre_ln()
+        for r in range(self.P):
+            self.attn(r)
+
+    def mlp_phase(self):
+        for r in range(self.P):
+            self.mlp_col(r)
+            self.mlp_row(r)
+
+    def step(self):
+        self.attention_phase()
+        self.reduce1()
+        self.mlp_phase()
+        self.reduce2()

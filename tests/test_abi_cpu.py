@@ -1,0 +1,176 @@
+"""The C-ABI library without a GPU: it loads, exports every function tp_shard.h declares,
+and rejects every invalid argument before any HIP call (so these calls launch nothing).
+
+Pointers here are fake, never dereferenced addresses; the module is skipped where a GPU is
+visible so that a validation bug can never turn into a launch on a real device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT, gpu_available
+
+pytestmark = pytest.mark.skipif(gpu_available(), reason="host-only validation tests")
+
+HEADER = os.path.join(ROOT, "include", "tp_shard.h")
+
+
+@pytest.fixture(scope="module")
+def tp():
+    from megatron_tensor_transformer_linear_amd import _build
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build_library()
+    from megatron_tensor_transformer_linear_amd import tp as mod
+    return mod
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_head_shard",
+              "tp_partial_reduce_residual_ln", "tp_attn_workspace_bytes", "tp_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(tp):
+    lib = ctypes.CDLL(tp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (tp_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+    assert set(tp.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings(tp):
+    for code in range(0, -9, -1):
+        s = tp.tp_status_string(code)
+        assert s.startswith("TP_OK" if code == 0 else "TP_ERR_")
+    assert tp.tp_status_string(-100) == "unknown tp_status"
+
+
+P = 0x10000  # fake, 256-byte aligned, never dereferenced
+
+
+def col(tp, **kw):
+    a = dict(X=P, W=P, Y=P, ldy=512, seq=64, H=256, N=1024, rank=0, world=2,
+             act=tp.TP_ACT_GELU_TANH, dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_col_linear_gelu(a["X"], a["W"], a["Y"], a["ldy"], a["seq"], a["H"], a["N"],
+                                     a["rank"], a["world"], a["act"], a["dtype"], a["stream"])
+
+
+def row(tp, **kw):
+    a = dict(X=P, ldx=1024, W=P, Z=P, seq=64, K=1024, N=256, rank=1, world=2, dtype=tp.TP_BF16,
+             stream=None)
+    a.update(kw)
+    return tp.lib.tp_row_linear_partial(a["X"], a["ldx"], a["W"], a["Z"], a["seq"], a["K"], a["N"],
+                                        a["rank"], a["world"], a["dtype"], a["stream"])
+
+
+def attn(tp, **kw):
+    a = dict(Xn=P, Wqkv=P, Wo=P, Z=P, batch=2, seq=64, H=1024, nh=8, d=128, rank=0, world=4,
+             causal=1, dtype=tp.TP_BF16, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return tp.lib.tp_attn_head_shard(a["Xn"], a["Wqkv"], a["Wo"], a["Z"], a["batch"], a["seq"],
+                                     a["H"], a["nh"], a["d"], a["rank"], a["world"], a["causal"],
+                                     a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+def red(tp, **kw):
+    a = dict(parts=P, n=4, stride=64 * 256, res=P, g=P, b=P, eps=1e-5, h=P, y=P, rows=64, H=256,
+             dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_partial_reduce_residual_ln(a["parts"], a["n"], a["stride"], a["res"], a["g"],
+                                                a["b"], a["eps"], a["h"], a["y"], a["rows"],
+                                                a["H"], a["dtype"], a["stream"])
+
+
+CASES = [
+    # column-parallel linear
+    ("col null X", col, dict(X=None), "TP_ERR_NULL"),
+    ("col null W", col, dict(W=None), "TP_ERR_NULL"),
+    ("col null Y", col, dict(Y=None), "TP_ERR_NULL"),
+    ("col bad dtype", col, dict(dtype=7), "TP_ERR_DTYPE"),
+    ("col bad act", col, dict(act=3), "TP_ERR_DTYPE"),
+    ("col world 0", col, dict(world=0), "TP_ERR_RANK"),
+    ("col rank = world", col, dict(rank=2), "TP_ERR_RANK"),
+    ("col rank < 0", col, dict(rank=-1), "TP_ERR_RANK"),
+    ("col seq 0", col, dict(seq=0), "TP_ERR_SHAPE"),
+    ("col H 0", col, dict(H=0), "TP_ERR_SHAPE"),
+    ("col N negative", col, dict(N=-8), "TP_ERR_SHAPE"),
+    ("col N % world", col, dict(N=1024, world=3, rank=0, ldy=1024), "TP_ERR_DIVISIBLE"),
+    ("col ldy < N/world", col, dict(ldy=504), "TP_ERR_SHAPE"),
+    ("col misaligned X", col, dict(X=P + 2), "TP_ERR_ALIGN"),
+    ("col misaligned Y", col, dict(Y=P + 8), "TP_ERR_ALIGN"),
+    ("col H % 8", col, dict(H=252), "TP_ERR_ALIGN"),
+    ("col N/world % 8", col, dict(N=1028, world=2, ldy=1028), "TP_ERR_ALIGN"),
+    ("col ldy % 8", col, dict(ldy=516), "TP_ERR_ALIGN"),
+    # row-parallel partial
+    ("row null X", row, dict(X=None), "TP_ERR_NULL"),
+    ("row null Z", row, dict(Z=None), "TP_ERR_NULL"),
+    ("row bad dtype", row, dict(dtype=2), "TP_ERR_DTYPE"),
+    ("row rank > world", row, dict(rank=5), "TP_ERR_RANK"),
+    ("row K 0", row, dict(K=0), "TP_ERR_SHAPE"),
+    ("row ldx < K", row, dict(ldx=1016), "TP_ERR_SHAPE"),
+    ("row K % world", row, dict(K=1024, world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("row K/world % 8", row, dict(K=1032, ldx=1032, world=2), "TP_ERR_ALIGN"),
+    ("row misaligned W", row, dict(W=P + 4), "TP_ERR_ALIGN"),
+    ("row ldx % 8", row, dict(ldx=1028), "TP_ERR_ALIGN"),
+    # attention-head shard
+    ("attn null Wo", attn, dict(Wo=None), "TP_ERR_NULL"),
+    ("attn f32", attn, dict(dtype=0), "TP_ERR_DTYPE"),
+    ("attn bad rank", attn, dict(rank=4), "TP_ERR_RANK"),
+    ("attn H != heads*d", attn, dict(H=1000), "TP_ERR_SHAPE"),
+    ("attn head_dim 64", attn, dict(d=64, nh=16), "TP_ERR_SHAPE"),
+    ("attn seq 0", attn, dict(seq=0), "TP_ERR_SHAPE"),
+    ("attn heads % world", attn, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("attn no workspace", attn, dict(ws=None), "TP_ERR_WORKSPACE"),
+    ("attn small workspace", attn, dict(wsb=1000), "TP_ERR_WORKSPACE"),
+    ("attn misaligned workspace", attn, dict(ws=P + 16), "TP_ERR_ALIGN"),
+    ("attn misaligned Xn", attn, dict(Xn=P + 2), "TP_ERR_ALIGN"),
+    # reduce + residual + LN
+    ("reduce bad dtype", red, dict(dtype=9), "TP_ERR_DTYPE"),
+    ("reduce negative parts", red, dict(n=-1), "TP_ERR_SHAPE"),
+    ("reduce null parts", red, dict(parts=None), "TP_ERR_NULL"),
+    ("reduce nothing to read", red, dict(n=0, parts=None, res=None), "TP_ERR_NULL"),
+    ("reduce gamma without y", red, dict(y=None), "TP_ERR_NULL"),
+    ("reduce no output", red, dict(g=None, h=None), "TP_ERR_NULL"),
+    ("reduce rows 0", red, dict(rows=0), "TP_ERR_SHAPE"),
+    ("reduce H too large", red, dict(H=65544, stride=64 * 65544), "TP_ERR_SHAPE"),
+    ("reduce negative eps", red, dict(eps=-1.0), "TP_ERR_SHAPE"),
+    ("reduce NaN eps", red, dict(eps=float("nan")), "TP_ERR_SHAPE"),
+    ("reduce stride too small", red, dict(stride=64 * 256 - 4), "TP_ERR_SHAPE"),
+    ("reduce H % 8", red, dict(H=252, stride=64 * 252), "TP_ERR_ALIGN"),
+    ("reduce stride % 4", red, dict(stride=64 * 256 + 2), "TP_ERR_ALIGN"),
+    ("reduce misaligned residual", red, dict(res=P + 8), "TP_ERR_ALIGN"),
+    ("reduce misaligned y", red, dict(y=P + 2), "TP_ERR_ALIGN"),
+]
+
+
+@pytest.mark.parametrize("name,fn,kw,expect", CASES, ids=[c[0] for c in CASES])
+def test_validation_rejects_before_launch(tp, name, fn, kw, expect):
+    assert fn(tp, **kw) == getattr(tp, expect)
+
+
+def test_workspace_bytes(tp):
+    T, nb = 2 * 64, (8 // 4) * 128
+    expect = (T * 3 * nb * 2 + T * nb * 2 + 255) // 256 * 256
+    assert tp.tp_attn_workspace_bytes(2, 64, 1024, 8, 128, 4, tp.TP_BF16) == expect
+    assert tp.tp_attn_workspace_bytes(2, 64, 1024, 8, 128, 3, tp.TP_BF16) == 0
+    assert tp.tp_attn_workspace_bytes(2, 64, 1024, 8, 128, 4, tp.TP_F32) == 0
+    assert tp.tp_attn_workspace_bytes(2, 64, 1000, 8, 128, 4, tp.TP_BF16) == 0
+
+
+def test_python_wrapper_raises(tp):
+    with pytest.raises(tp.TPError) as e:
+        tp.tp_col_linear_gelu(P, P, P, 512, 64, 256, 1024, 2, 2, 1, tp.TP_BF16, stream=0)
+    assert e.value.status == tp.TP_ERR_RANK

@@ -1,0 +1,506 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 CPU oracle.
+
+Bit-exact where the result is exact in both (shard extraction, concatenation, integer
+GEMMs); otherwise the tolerance rule of gpu_helpers.check.  Reduced-size variants of the
+five workloads (several tiles plus ragged tails) are compared element by element; the
+full-size workloads, launched exactly as the bench launches them, on sampled rows."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.tp_oracle as O
+from gpu_helpers import check, check_exact, dev, dev_values, host, sample_rows, say
+from workloads import generate, get_config
+from workloads.configs import small_variant
+from workloads.synth import from_values, integer_matrix, random_affine
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib(gpu):
+    from megatron_tensor_transformer_linear_amd import pipeline, tp
+    torch.cuda.set_device(0)
+    return tp, pipeline
+
+
+def _qkv_bits(t):
+    return np.ascontiguousarray(np.hstack([t["Wq"].data, t["Wk"].data, t["Wv"].data]))
+
+
+def _qkv_values(t):
+    return np.hstack([t["Wq"].values(), t["Wk"].values(), t["Wv"].values()])
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ============================================================== bit-exact indexing pins
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("world", [1, 2, 4])
+def test_column_shard_onehot_exact(lib, dtype, world):
+    """X = one-hot rows, so Y[t, j] = W[k(t), r N/P + j]: any misplaced shard, wrong offset,
+    transposed slice or wrong leading dimension shows as a wrong value."""
+    tp, pl = lib
+    T, H, N = 300, 272, 784 if world != 4 else 800
+    rng = np.random.Generator(np.random.PCG64(100 + world))
+    X = np.zeros((T, H), np.float32)
+    X[np.arange(T), (np.arange(T) * 37) % H] = 1.0
+    Wv = from_values("W", rng.standard_normal((H, N)).astype(np.float32), dtype).values()
+    Xd, Wd = dev_values(X, dtype), dev_values(Wv, dtype)
+    Yfull = torch.full((T, N), -7.0, dtype=Xd.dtype, device=Xd.device)
+    nl = N // world
+    for r in range(world):
+        say(f"  column one-hot dtype={dtype} world={world} rank={r} T={T} H={H} N={N}")
+        tp.tp_col_linear_gelu(Xd, Wd, Yfull[:, r * nl:], N, T, H, N, r, world, tp.TP_ACT_NONE,
+                              tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    ref = O.concat_columns([O.col_linear(X, Wv, r, world) for r in range(world)])
+    check_exact(f"concat world={world}", Yfull, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_column_writes_only_its_block(lib, dtype):
+    """Only columns [0, N/P) of the rank's output view are written; the rest of Yfull keeps
+    its sentinel."""
+    tp, pl = lib
+    T, H, N, P = 100, 64, 512, 4
+    rng = np.random.Generator(np.random.PCG64(7))
+    Xd = dev_values(rng.standard_normal((T, H)), dtype)
+    Wd = dev_values(rng.standard_normal((H, N)), dtype)
+    Y = torch.full((T, N), 3.0, dtype=Xd.dtype, device=Xd.device)
+    say(f"  column writes only rank 2 block dtype={dtype}")
+    tp.tp_col_linear_gelu(Xd, Wd, Y[:, 2 * 128:], N, T, H, N, 2, P, tp.TP_ACT_GELU_TANH,
+                          tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    Yh = host(Y)
+    assert np.all(Yh[:, :256] == 3.0) and np.all(Yh[:, 384:] == 3.0)
+    assert not np.all(Yh[:, 256:384] == 3.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("world", [2, 4, 8])
+def test_row_partials_integer_exact(lib, dtype, world):
+    """Integer X in {-1,0,1} and W in {-2..2}: every partial and their sum are exact
+    integers below 2^24, so the GPU must match the oracle bit for bit."""
+    tp, pl = lib
+    T, K, N = 260, 1088 if world != 8 else 1152, 392
+    rng = np.random.Generator(np.random.PCG64(200 + world))
+    X = integer_matrix(rng, (T, K), -1, 1, dtype)
+    W = integer_matrix(rng, (K, N), -2, 2, dtype)
+    Xd, Wd = dev(X), dev(W)
+    sh = pl.LinearShard(Xd, Wd, world, dtype, col_ranks=())
+    say(f"  row partials integer dtype={dtype} world={world} T={T} K={K} N={N}")
+    sh.step()
+    _sync()
+    parts = [O.row_linear_partial(X.values(), W.values(), r, world) for r in range(world)]
+    for r in range(world):
+        check_exact(f"partial rank {r}", sh.parts[r], parts[r], "f32")
+    check_exact("sum of partials", sh.Z, O.reduce_partials(parts), "f32")
+
+
+@pytest.mark.parametrize("world", [2, 4])
+def test_mlp_concat_integer_exact(lib, world):
+    """Sparse integer X (8 nonzeros per row) and integer A: the column outputs are small
+    integers, exact in bf16, so the concatenated hidden activation (no activation) is
+    bit-exact; the row stage then reads exactly that buffer."""
+    tp, pl = lib
+    T, H, F = 300, 264, 1088
+    rng = np.random.Generator(np.random.PCG64(300 + world))
+    X = integer_matrix(rng, (T, H), -1, 1, "bf16", nnz_per_row=8)
+    A = integer_matrix(rng, (H, F), -2, 2, "bf16")
+    Xd, Ad = dev(X), dev(A)
+    Yfull = torch.empty(T, F, dtype=torch.bfloat16, device="cuda:0")
+    fl = F // world
+    for r in range(world):
+        say(f"  mlp concat integer world={world} rank={r}")
+        tp.tp_col_linear_gelu(Xd, Ad, Yfull[:, r * fl:], F, T, H, F, r, world, tp.TP_ACT_NONE,
+                              tp.TP_BF16)
+    _sync()
+    ref = O.concat_columns([O.col_linear(X.values(), A.values(), r, world) for r in range(world)])
+    check_exact("hidden concat", Yfull, ref, "bf16")
+
+
+# ============================================================== reduced-size workloads
+def test_small_mlp_f32(lib):
+    tp, pl = lib
+    cfg = small_variant("mlp_f32_tp2")
+    t = generate(cfg)
+    sh = pl.MLPShard(dev(t["X"]), dev(t["A"]), dev(t["B"]), cfg.world, "f32", residual_ln=False)
+    say(f"  small fp32 MLP {cfg}")
+    sh.step()
+    _sync()
+    X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
+    Y = O.concat_columns([O.col_linear(X, A, r, cfg.world, "gelu_tanh") for r in range(cfg.world)])
+    check("hidden (GeLU)", sh.Yfull, Y, "f32")
+    parts = [O.mlp_shard(X, A, B, r, cfg.world) for r in range(cfg.world)]
+    for r in range(cfg.world):
+        check(f"partial rank {r}", sh.parts[r], parts[r], "f32")
+    check("Z", sh.Z, O.reduce_partials(parts), "f32")
+
+
+def test_small_linear_bf16(lib):
+    tp, pl = lib
+    cfg = small_variant("linear_bf16_tp2")
+    t = generate(cfg)
+    sh = pl.LinearShard(dev(t["X"]), dev(t["W"]), cfg.world, "bf16", col_ranks=(0, 1))
+    say(f"  small bf16 linear {cfg}")
+    sh.step()
+    _sync()
+    X, W = t["X"].values(), t["W"].values()
+    for r in (0, 1):
+        check(f"column block rank {r}", sh.Ycol[r], O.col_linear(X, W, r, cfg.world), "bf16")
+    parts = [O.row_linear_partial(X, W, r, cfg.world) for r in range(cfg.world)]
+    for r in range(cfg.world):
+        check(f"row partial rank {r}", sh.parts[r], parts[r], "bf16")
+    check("Z", sh.Z, O.reduce_partials(parts), "bf16")
+
+
+@pytest.mark.parametrize("affine", [False, True])
+def test_small_mlp_bf16(lib, affine):
+    tp, pl = lib
+    cfg = small_variant("mlp_bf16_tp4")
+    t = generate(cfg)
+    if affine:
+        t.update(random_affine(cfg, 5))
+    sh = pl.MLPShard(dev(t["X"]), dev(t["A"]), dev(t["B"]), cfg.world, "bf16",
+                     gamma=dev(t["gamma"]), beta=dev(t["beta"]), eps=cfg.eps)
+    say(f"  small bf16 MLP affine={affine} {cfg}")
+    sh.step()
+    _sync()
+    X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
+    Y = O.concat_columns([O.col_linear(X, A, r, cfg.world, "gelu_tanh") for r in range(cfg.world)])
+    check("hidden (GeLU)", sh.Yfull, Y, "bf16")
+    parts = [O.mlp_shard(X, A, B, r, cfg.world) for r in range(cfg.world)]
+    for r in range(cfg.world):
+        check(f"partial rank {r}", sh.parts[r], parts[r], "bf16")
+    h, y = O.reduce_residual_layernorm(parts, X, t["gamma"].values(), t["beta"].values(), cfg.eps)
+    check("h = X + sum", sh.h, h, "bf16")
+    check("y = LN(h)", sh.y, y, "bf16")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_small_attention(lib, causal):
+    tp, pl = lib
+    cfg = small_variant("attn_bf16_tp4").with_(causal=causal)
+    t = generate(cfg)
+    Xn = t["X"].values()
+    Wqkv = _qkv_values(t)
+    Wo = t["Wo"].values()
+    sh = pl.AttnShard(dev(t["X"]), dev_values(Wqkv, "bf16"), dev(t["Wo"]), cfg.world, cfg.batch,
+                      cfg.seq, cfg.n_heads, cfg.head_dim, causal)
+    H, nb = cfg.hidden, (cfg.n_heads // cfg.world) * cfg.head_dim
+    parts = []
+    for r in range(cfg.world):
+        say(f"  small attention causal={causal} rank={r} {cfg}")
+        sh.rank(r)
+        _sync()
+        qkv, A = sh.workspace_views()
+        h0 = r * nb
+        ref_qkv = np.hstack([O.matmul(Xn, Wqkv[:, b * H + h0: b * H + h0 + nb]) for b in range(3)])
+        check(f"QKV rank {r}", qkv, ref_qkv, "bf16")
+        check(f"heads rank {r}", A, O.attention_heads(Xn, Wqkv, cfg.n_heads, cfg.head_dim, r,
+                                                     cfg.world, cfg.batch, cfg.seq, causal), "bf16")
+        parts.append(O.attn_head_shard(Xn, Wqkv, Wo, cfg.n_heads, cfg.head_dim, r, cfg.world,
+                                       cfg.batch, cfg.seq, causal))
+        check(f"O partial rank {r}", sh.parts[r], parts[r], "bf16")
+    sh.reduce()
+    _sync()
+    check("sum of partials", sh.Z, O.reduce_partials(parts), "bf16")
+
+
+def _block_runner(pl, cfg, t):
+    return pl.BlockShard(dev(t["X"]), dev_values(_qkv_values(t), "bf16"), dev(t["Wo"]),
+                         dev(t["W1"]), dev(t["W2"]), dev(t["gamma"]), dev(t["beta"]),
+                         dev(t["gamma"]), dev(t["beta"]), cfg.world, cfg.batch, cfg.seq,
+                         cfg.n_heads, cfg.head_dim, cfg.causal, cfg.eps)
+
+
+def _block_ref(cfg, t, rows=None):
+    g, b = t["gamma"].values(), t["beta"].values()
+    return O.block_shard(t["X"].values(), _qkv_values(t), t["Wo"].values(), t["W1"].values(),
+                         t["W2"].values(), g, b, g, b, n_heads=cfg.n_heads,
+                         head_dim=cfg.head_dim, world=cfg.world, batch=cfg.batch, seq=cfg.seq,
+                         causal=cfg.causal, eps=cfg.eps, rows=rows)
+
+
+def test_small_block(lib):
+    tp, pl = lib
+    cfg = small_variant("block_bf16_tp8")
+    t = generate(cfg)
+    sh = _block_runner(pl, cfg, t)
+    ref = _block_ref(cfg, t)
+    say(f"  small block: pre-LN + attention phase {cfg}")
+    sh.attention_phase()
+    _sync()
+    check("xn = LN(X)", sh.xn, ref["xn"], "bf16")
+    for r in range(cfg.world):
+        check(f"attention partial rank {r}", sh.parts[r], ref["attn_parts"][r], "bf16")
+    say("  small block: reduce1 + MLP phase + reduce2")
+    sh.reduce1()
+    sh.mlp_phase()
+    _sync()
+    check("h", sh.h, ref["h"], "bf16")
+    check("hn", sh.hn, ref["hn"], "bf16")
+    for r in range(cfg.world):
+        check(f"MLP partial rank {r}", sh.parts[r], ref["mlp_parts"][r], "bf16")
+    sh.reduce2()
+    _sync()
+    check("out", sh.out, ref["out"], "bf16")
+
+
+def test_block_deterministic(lib):
+    tp, pl = lib
+    cfg = small_variant("block_bf16_tp8")
+    t = generate(cfg)
+    sh = _block_runner(pl, cfg, t)
+    say("  block determinism: two steps")
+    sh.step()
+    _sync()
+    first = sh.out.clone()
+    sh.step()
+    _sync()
+    assert torch.equal(first.view(torch.int16), sh.out.view(torch.int16))
+
+
+# ============================================================== edge cases
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,H,N,world,rank", [
+    (1, 8, 8, 1, 0),          # smallest everything
+    (1, 264, 16, 2, 1),       # single row, narrow shard
+    (257, 64, 520, 1, 0),     # one row past a tile, world 1
+    (33, 4104, 264, 3, 2),    # K past 64 ragged, odd world, last rank
+    (513, 128, 4096, 8, 7),   # wide N, many ranks
+])
+def test_column_edge_shapes(lib, dtype, T, H, N, world, rank):
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(T * 7 + N))
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((H, N)) / np.sqrt(H)).astype(np.float32)
+    Xd, Wd = dev_values(X, dtype), dev_values(W, dtype)
+    Xv, Wv = host(Xd), host(Wd)
+    nl = N // world
+    Y = torch.empty(T, nl + 8, dtype=Xd.dtype, device=Xd.device)  # ldy > width
+    say(f"  column edge dtype={dtype} T={T} H={H} N={N} world={world} rank={rank}")
+    tp.tp_col_linear_gelu(Xd, Wd, Y, nl + 8, T, H, N, rank, world, tp.TP_ACT_GELU_TANH,
+                          tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    check("column", Y[:, :nl], O.col_linear(Xv, Wv, rank, world, "gelu_tanh"), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,K,N,world,rank", [
+    (1, 8, 8, 1, 0),
+    (5, 16, 24, 2, 1),
+    (300, 1040, 136, 2, 0),   # K/world = 520: ragged K tile
+    (64, 6144, 264, 8, 5),
+])
+def test_row_edge_shapes(lib, dtype, T, K, N, world, rank):
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(T * 11 + K))
+    X = rng.standard_normal((T, K + 16)).astype(np.float32)  # ldx > K
+    W = (rng.standard_normal((K, N)) / np.sqrt(K)).astype(np.float32)
+    Xd, Wd = dev_values(X, dtype), dev_values(W, dtype)
+    Xv, Wv = host(Xd), host(Wd)
+    Z = torch.empty(T, N, dtype=torch.float32, device=Xd.device)
+    say(f"  row edge dtype={dtype} T={T} K={K} N={N} world={world} rank={rank}")
+    tp.tp_row_linear_partial(Xd, K + 16, Wd, Z, T, K, N, rank, world,
+                             tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    check("row partial", Z, O.row_linear_partial(Xv[:, :K], Wv, rank, world), dtype)
+
+
+@pytest.mark.parametrize("batch,seq,n_heads,world,causal", [
+    (1, 1, 2, 1, True),        # one token
+    (3, 65, 4, 2, True),       # one key past a key block, three sequences
+    (2, 130, 2, 2, False),     # one query past a query block, full attention
+    (1, 257, 8, 8, True),      # one head per rank
+])
+def test_attention_edge_shapes(lib, batch, seq, n_heads, world, causal):
+    tp, pl = lib
+    d = 128
+    H = n_heads * d
+    rng = np.random.Generator(np.random.PCG64(seq * 13 + n_heads))
+    Xn = rng.standard_normal((batch * seq, H)).astype(np.float32)
+    Wqkv = (rng.standard_normal((H, 3 * H)) / np.sqrt(H)).astype(np.float32)
+    Wo = (rng.standard_normal((H, H)) / np.sqrt(H)).astype(np.float32)
+    Xd, Wqd, Wod = dev_values(Xn, "bf16"), dev_values(Wqkv, "bf16"), dev_values(Wo, "bf16")
+    Xv, Wqv, Wov = host(Xd), host(Wqd), host(Wod)
+    sh = pl.AttnShard(Xd, Wqd, Wod, world, batch, seq, n_heads, d, causal)
+    for r in range(world):
+        say(f"  attention edge batch={batch} seq={seq} heads={n_heads} world={world} rank={r} causal={causal}")
+        sh.rank(r)
+        _sync()
+        _, A = sh.workspace_views()
+        check(f"heads rank {r}", A, O.attention_heads(Xv, Wqv, n_heads, d, r, world, batch, seq,
+                                                     causal), "bf16")
+        check(f"partial rank {r}", sh.parts[r], O.attn_head_shard(Xv, Wqv, Wov, n_heads, d, r,
+                                                                  world, batch, seq, causal), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,H,n_parts,residual,ln", [
+    (5, 8, 0, True, True),        # plain LayerNorm of a narrow row
+    (300, 12288, 1, True, True),  # one partial, wide row
+    (64, 4104, 3, False, True),   # no residual, ragged vector tail
+    (17, 65536, 2, True, True),   # widest supported row (1024-thread path)
+    (100, 256, 8, True, False),   # sum only, h_out
+])
+def test_reduce_edge_cases(lib, dtype, rows, H, n_parts, residual, ln):
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(rows * 3 + H + n_parts))
+    parts = (rng.standard_normal((max(n_parts, 1), rows, H)) * 2).astype(np.float32)
+    R = (rng.standard_normal((rows, H)) + 0.5).astype(np.float32)
+    g = (1 + 0.5 * rng.standard_normal(H)).astype(np.float32)
+    b = (0.5 * rng.standard_normal(H)).astype(np.float32)
+    Pd = torch.from_numpy(parts).to("cuda:0")
+    Rd, gd, bd = dev_values(R, dtype), dev_values(g, dtype), dev_values(b, dtype)
+    hd = torch.empty(rows, H, dtype=Rd.dtype, device="cuda:0")
+    yd = torch.empty_like(hd)
+    say(f"  reduce edge dtype={dtype} rows={rows} H={H} parts={n_parts} residual={residual} ln={ln}")
+    tp.tp_partial_reduce_residual_ln(Pd if n_parts else None, n_parts, rows * H,
+                                     Rd if residual else None, gd if ln else None,
+                                     bd if ln else None, 1e-5, hd, yd if ln else None, rows, H,
+                                     tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    h, y = O.reduce_residual_layernorm(list(parts[:n_parts]), host(Rd) if residual else None,
+                                       host(gd) if ln else None, host(bd) if ln else None, 1e-5)
+    check("h", hd, h, dtype)
+    if ln:
+        check("y", yd, y, dtype)
+
+
+def test_errors_leave_outputs_untouched(lib):
+    tp, pl = lib
+    Xd = torch.ones(64, 256, dtype=torch.bfloat16, device="cuda:0")
+    Wd = torch.ones(256, 1024, dtype=torch.bfloat16, device="cuda:0")
+    Y = torch.full((64, 512), 5.0, dtype=torch.bfloat16, device="cuda:0")
+    say("  invalid calls on real buffers")
+    with pytest.raises(tp.TPError):
+        tp.tp_col_linear_gelu(Xd, Wd, Y, 512, 64, 256, 1024, 2, 2, 0, tp.TP_BF16)
+    with pytest.raises(tp.TPError):
+        tp.tp_col_linear_gelu(Xd, Wd, Y, 500, 64, 256, 1000, 0, 2, 0, tp.TP_BF16)
+    _sync()
+    assert torch.all(Y == 5.0)
+
+
+# ============================================================== full-size workloads
+FULL = pytest.mark.timeout(600)
+
+
+@FULL
+def test_full_mlp_f32(lib):
+    tp, pl = lib
+    cfg = get_config("mlp_f32_tp2")
+    t = generate(cfg)
+    sh = pl.MLPShard(dev(t["X"]), dev(t["A"]), dev(t["B"]), cfg.world, "f32", residual_ln=False)
+    say(f"  full fp32 MLP {cfg.name}")
+    sh.step()
+    _sync()
+    X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
+    Y = O.concat_columns([O.col_linear(X, A, r, cfg.world, "gelu_tanh") for r in range(cfg.world)])
+    check("hidden (GeLU)", sh.Yfull, Y, "f32")
+    parts = [O.mlp_shard(X, A, B, r, cfg.world) for r in range(cfg.world)]
+    for r in range(cfg.world):
+        check(f"partial rank {r}", sh.parts[r], parts[r], "f32")
+    check("Z", sh.Z, O.reduce_partials(parts), "f32")
+
+
+@FULL
+def test_full_linear_bf16(lib):
+    tp, pl = lib
+    cfg = get_config("linear_bf16_tp2")
+    t = generate(cfg)
+    sh = pl.LinearShard(dev(t["X"]), dev(t["W"]), cfg.world, "bf16", col_ranks=(0,))
+    say(f"  full bf16 linear {cfg.name}")
+    sh.step()
+    _sync()
+    rows = sample_rows(cfg.tokens, 0, 1)
+    X, W = t["X"].values(), t["W"].values()
+    check("column rank 0 (rows)", sh.Ycol[0][rows], O.col_linear(X, W, 0, 2, rows=rows), "bf16")
+    parts = [O.row_linear_partial(X, W, r, 2, rows=rows) for r in range(2)]
+    for r in range(2):
+        check(f"row partial {r} (rows)", sh.parts[r][rows], parts[r], "bf16")
+    check("Z (rows)", sh.Z[rows], O.reduce_partials(parts), "bf16")
+
+
+@FULL
+def test_full_mlp_bf16(lib):
+    tp, pl = lib
+    cfg = get_config("mlp_bf16_tp4")
+    t = generate(cfg)
+    sh = pl.MLPShard(dev(t["X"]), dev(t["A"]), dev(t["B"]), cfg.world, "bf16",
+                     gamma=dev(t["gamma"]), beta=dev(t["beta"]), eps=cfg.eps)
+    say(f"  full bf16 MLP {cfg.name}")
+    sh.step()
+    _sync()
+    rows = sample_rows(cfg.tokens, cfg.seq, 2)
+    X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
+    Y = O.concat_columns([O.col_linear(X, A, r, cfg.world, "gelu_tanh", rows)
+                          for r in range(cfg.world)])
+    check("hidden (rows)", sh.Yfull[rows], Y, "bf16")
+    parts = [O.mlp_shard(X, A, B, r, cfg.world, rows=rows) for r in range(cfg.world)]
+    for r in range(cfg.world):
+        check(f"partial rank {r} (rows)", sh.parts[r][rows], parts[r], "bf16")
+    h, y = O.reduce_residual_layernorm(parts, X[rows], t["gamma"].values(), t["beta"].values(),
+                                       cfg.eps)
+    check("h (rows)", sh.h[rows], h, "bf16")
+    check("y (rows)", sh.y[rows], y, "bf16")
+
+
+@FULL
+def test_full_attention(lib):
+    tp, pl = lib
+    cfg = get_config("attn_bf16_tp4")
+    t = generate(cfg)
+    Xn, Wqkv, Wo = t["X"].values(), _qkv_values(t), t["Wo"].values()
+    sh = pl.AttnShard(dev(t["X"]), dev_values(Wqkv, "bf16"), dev(t["Wo"]), cfg.world, cfg.batch,
+                      cfg.seq, cfg.n_heads, cfg.head_dim, cfg.causal)
+    say(f"  full attention {cfg.name}")
+    sh.step()
+    _sync()
+    rows = sample_rows(cfg.tokens, cfg.seq, 3)
+    _, A = sh.workspace_views()
+    r_last = cfg.world - 1
+    check(f"heads rank {r_last} (rows)", A[rows],
+          O.attention_heads(Xn, Wqkv, cfg.n_heads, cfg.head_dim, r_last, cfg.world, cfg.batch,
+                            cfg.seq, True, rows), "bf16")
+    parts = []
+    for r in range(cfg.world):
+        parts.append(O.attn_head_shard(Xn, Wqkv, Wo, cfg.n_heads, cfg.head_dim, r, cfg.world,
+                                       cfg.batch, cfg.seq, True, rows))
+        check(f"partial rank {r} (rows)", sh.parts[r][rows], parts[r], "bf16")
+    check("sum (rows)", sh.Z[rows], O.reduce_partials(parts), "bf16")
+
+
+@FULL
+def test_full_block(lib):
+    tp, pl = lib
+    cfg = get_config("block_bf16_tp8")
+    t = generate(cfg)
+    say(f"  full block {cfg.name}: inputs generated")
+    sh = _block_runner(pl, cfg, t)
+    sh.attention_phase()
+    _sync()
+    T, S = cfg.tokens, cfg.seq
+    rows = np.array([0, 1, 127, 128, 1000, 2047, 3 * S + 5, 3 * S + 1500, 4 * S - 1])
+    attn_parts = [host(sh.parts[r][rows]) for r in range(cfg.world)]
+    xn = host(sh.xn[rows])
+    say("  full block: attention phase done, running reduce + MLP")
+    sh.reduce1()
+    sh.mlp_phase()
+    sh.reduce2()
+    _sync()
+    say("  full block: GPU done, computing sampled oracle rows")
+    ref = _block_ref(cfg, t, rows)
+    check("xn (rows)", xn, ref["xn"], "bf16")
+    for r in range(cfg.world):
+        check(f"attention partial {r} (rows)", attn_parts[r], ref["attn_parts"][r], "bf16")
+    check("h (rows)", sh.h[rows], ref["h"], "bf16")
+    check("hn (rows)", sh.hn[rows], ref["hn"], "bf16")
+    for r in range(cfg.world):
+        check(f"MLP partial {r} (rows)", sh.parts[r][rows], ref["mlp_parts"][r], "bf16")
+    check("out (rows)", sh.out[rows], ref["out"], "bf16")

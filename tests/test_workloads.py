@@ -26,13 +26,16 @@ def test_bf16_decode_exact():
     assert np.array_equal(f32_to_bf16_bits(v), b)
 
 
-def test_chunked_draw_equals_single_draw(monkeypatch):
-    cfg = small_variant("linear_bf16_tp2")
-    whole = generate(cfg)
-    monkeypatch.setattr(synth, "_CHUNK", 1000)
-    chunked = generate(cfg)
-    for k in whole:
-        assert np.array_equal(whole[k].data, chunked[k].data)
+def test_thread_count_does_not_change_values(monkeypatch):
+    cfg = small_variant("linear_bf16_tp2").with_(tokens=3000)
+    monkeypatch.setattr(synth, "CHUNK_ELEMS", 4096)
+    a = generate(cfg, threads=1)
+    b = generate(cfg, threads=7)
+    for k in a:
+        assert np.array_equal(a[k].data, b[k].data)
+    c = generate(cfg, only={"W"})
+    assert set(c) >= {"W"} and "X" not in c
+    assert np.array_equal(c["W"].data, a["W"].data)
 
 
 def test_deterministic_and_distinct_seeds():

@@ -1,22 +1,25 @@
 """Seeded generation of the workloads' inputs.
 
-Recipe: numpy ``Generator(PCG64(seed))``; draws in the order ``Config.draws()``
-lists them, each at its full unsharded shape, ``standard_normal(dtype=float32)``
-multiplied by float32(1/sqrt(fan_in)) for weights.  bf16 workloads then round
-each float32 value to bfloat16 with round-to-nearest-even.  Large tensors are
-drawn in row chunks; a PCG64 stream consumed in chunks yields the same values as
-one draw of the whole tensor.
+Recipe: tensors are listed in the order ``Config.draws()`` gives (index i), each at
+its full unsharded shape and cut into row chunks of ``rows_per_chunk = max(1, 2**22 //
+cols)`` rows.  Chunk c of tensor i is ``Generator(PCG64(SeedSequence([seed, i, c])))
+.standard_normal(dtype=float32)``, multiplied by float32(1/sqrt(fan_in)) for weights.
+bf16 workloads then round each float32 value to bfloat16 (round to nearest, ties to
+even).  Chunks are independent streams, so they are drawn on a thread pool and the
+result does not depend on the number of threads.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Dict, Optional
 
 import numpy as np
 
 from .configs import Config
 
-_CHUNK = 1 << 24  # elements per draw chunk
+CHUNK_ELEMS = 1 << 22  # target elements per independently seeded chunk
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -49,29 +52,41 @@ class HostTensor:
         return self.data if self.dtype == "f32" else self.data.view(np.int16)
 
 
-def _draw(rng: np.random.Generator, shape, fan_in: int, dtype: str) -> np.ndarray:
+def _draw(seed: int, index: int, shape, fan_in: int, dtype: str,
+          threads: Optional[int] = None) -> np.ndarray:
     rows, cols = shape
     out = np.empty(shape, dtype=np.float32 if dtype == "f32" else np.uint16)
     scale = np.float32(1.0 / np.sqrt(fan_in)) if fan_in else None
-    step = max(1, _CHUNK // cols)
-    for r0 in range(0, rows, step):
-        r1 = min(rows, r0 + step)
-        x = rng.standard_normal(size=(r1 - r0, cols), dtype=np.float32)
+    step = max(1, CHUNK_ELEMS // cols)
+
+    def chunk(c: int) -> None:
+        r0, r1 = c * step, min(rows, (c + 1) * step)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, index, c])))
+        x = g.standard_normal(size=(r1 - r0, cols), dtype=np.float32)
         if scale is not None:
             x *= scale
         out[r0:r1] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    n = (rows + step - 1) // step
+    threads = threads or min(16, os.cpu_count() or 1)
+    if n == 1 or threads == 1:
+        for c in range(n):
+            chunk(c)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(chunk, range(n)))
     return out
 
 
-def generate(cfg: Config, only: Optional[set] = None) -> Dict[str, HostTensor]:
-    """All inputs of ``cfg`` in draw order.  Tensors not in ``only`` are still drawn
-    (to keep the stream aligned) but not kept."""
-    rng = np.random.Generator(np.random.PCG64(cfg.seed))
+def generate(cfg: Config, only: Optional[set] = None,
+             threads: Optional[int] = None) -> Dict[str, HostTensor]:
+    """All inputs of ``cfg`` (or only the named ones), keyed by name."""
     out: Dict[str, HostTensor] = {}
-    for name, shape, fan_in in cfg.draws():
-        arr = _draw(rng, shape, fan_in, cfg.dtype)
-        if only is None or name in only:
-            out[name] = HostTensor(name, cfg.dtype, tuple(shape), arr)
+    for index, (name, shape, fan_in) in enumerate(cfg.draws()):
+        if only is not None and name not in only:
+            continue
+        arr = _draw(cfg.seed, index, shape, fan_in, cfg.dtype, threads)
+        out[name] = HostTensor(name, cfg.dtype, tuple(shape), arr)
     if cfg.kind in ("mlp", "block", "attn"):
         ones = np.ones((cfg.hidden,), np.float32)
         zeros = np.zeros((cfg.hidden,), np.float32)
