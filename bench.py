@@ -40,15 +40,37 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_col_gelu_block_bf16_tp8_hbm_traffic.md")
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per launch of the MLP column GEMM from the committed counter summary, or
+    None when the kernel sources no longer hash to the digest the counters were taken at."""
+    import hashlib
+    try:
+        kv = dict(l.split(": ", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ": " in l
+                  and l.split(": ", 1)[0] in ("kernel_sources", "kernel_sources_sha256",
+                                              "traffic_bytes_per_launch"))
+        h = hashlib.sha256()
+        for f in kv["kernel_sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != kv["kernel_sources_sha256"].strip():
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, t, qkv_vals) -> dict:
     """The oracle as it stands, on a bounded row sample of the same block workload."""
     import oracle.tp_oracle as O
     S = cfg.seq
-    rows = np.unique(np.concatenate([np.linspace(0, S - 1, 24).astype(np.int64), [S - 1]]))
+    per_seq = np.unique(np.concatenate([np.linspace(0, S - 1, 256).astype(np.int64), [S - 1]]))
+    rows = np.concatenate([b * S + per_seq for b in range(cfg.batch)])
     g, b = t["gamma"].values(), t["beta"].values()
     args = (t["X"].values(), qkv_vals, t["Wo"].values(), t["W1"].values(), t["W2"].values(),
             g, b, g, b)
@@ -62,16 +84,18 @@ def cpu_baseline(cfg, t, qkv_vals) -> dict:
     H, P, d = cfg.hidden, cfg.world, cfg.head_dim
     hl = cfg.n_heads // P
     nb = hl * d
-    prefix = int(rows.max()) + 1
     R = len(rows)
-    per_rank = (2.0 * prefix * H * 2 * nb + 2.0 * R * H * nb
-                + sum(4.0 * d * (int(i) + 1) * hl for i in rows) + 2.0 * R * nb * H
+    pos = rows % S
+    kv_tokens = cfg.batch * (int(pos.max()) + 1)
+    per_rank = (2.0 * kv_tokens * H * 2 * nb + 2.0 * R * H * nb
+                + sum(4.0 * d * (int(i) + 1) * hl for i in pos) + 2.0 * R * nb * H
                 + 2.0 * 2.0 * R * H * (cfg.ffn // P))
     flops = per_rank * P
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
             "kind": "oracle",
-            "sample": (f"float64 oracle of the whole 8-rank block for {R} query rows of sequence 0 "
-                       f"(positions 0..{prefix - 1}, keys/values over the full causal prefix): "
+            "sample": (f"float64 oracle of the whole 8-rank block for {R} query rows "
+                       f"({len(per_seq)} positions spread over 0..{S - 1} in each of the "
+                       f"{cfg.batch} sequences; keys/values over the full causal prefixes): "
                        f"{flops / 1e9:.0f} GFLOP in {dt:.1f} s")}
 
 
@@ -81,6 +105,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain copy kernel over MIB mebibytes (reads and writes "
+                         "MIB each), the known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the tensor-parallel ranks are simulated in turn "
@@ -95,6 +122,15 @@ def main() -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 18  # float32 elements in MIB mebibytes
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads and writes MIB MiB each
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration kernel over {args.copy_calibration} MiB done")
     cfg = get_config(WORKLOAD)
     t0 = time.time()
     t = generate(cfg)
@@ -204,7 +240,7 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "flops_per_launch": col_flops,
             "avg_launch_ms": round(col_ms, 4),
         },
