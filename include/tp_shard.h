@@ -28,6 +28,9 @@
  *     failure returns TP_ERR_LAUNCH.
  *   - Alignment: pointers 16-byte aligned; leading dimensions, shard widths and the
  *     column offsets they imply are multiples of 8 elements.
+ *   - Size limits: the activation operand's row width (H of the column call, ldx of the row
+ *     call, H of the attention call) is at most 2^21 elements and the weight's row width (N)
+ *     at most 2^23 elements; larger values return TP_ERR_SHAPE.
  *   - Calls are re-entrant; concurrent calls on different streams may not write the same
  *     output.  Results are deterministic (fixed summation order, no atomics).
  */

@@ -89,19 +89,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const bool b_nvalid = b_nlog < N;
   const int64_t b_col = (b_nlog / g.b_blk) * g.b_blk_stride + (b_nlog % g.b_blk);
 
+  // Staging loads are raw buffer loads: the hardware returns zeros for any offset past the
+  // resource's byte range, so tile edges need neither branches nor selects.  A's resource
+  // covers the tile's rows (rows >= M fall outside it); B's resource is re-based at every K
+  // step and covers the remaining K rows of that step.  Chunks past K (for A) or past N (for
+  // B) are given an offset outside every range.
+  constexpr uint32_t OOB = 0x80000000u;
+  const int64_t a_rows = min((int64_t)BM, M - m0);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + m0 * lda), (short)0, (int)(a_rows * lda * 2), 0x00020000);
+  uint32_t a_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a_off[i] = (uint32_t)(((a_row + 32 * i) * lda + a_kc) * 2);
+  uint32_t b_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    b_off[i] = b_nvalid ? (uint32_t)(((b_row + 8 * i) * ldb + b_col) * 2) : OOB;
+
   uint4 ra[8], rb[8];
   auto gload = [&](int64_t k0) {
+    const bool a_kok = k0 + a_kc < K;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = m0 + a_row + 32 * i;
-      const int64_t k = k0 + a_kc;
-      ra[i] = (row < M && k < K) ? *(const uint4*)(A + row * lda + k) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i)
+      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rsrc_a, a_kok ? a_off[i] + (uint32_t)(k0 * 2) : OOB, 0, 0));
+    const int64_t k_rows = min((int64_t)BK, K - k0);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B + k0 * ldb), (short)0, (int)(k_rows * ldb * 2), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t k = k0 + b_row + 8 * i;
-      rb[i] = (b_nvalid && k < K) ? *(const uint4*)(B + k * ldb + b_col) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i)
+      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[i], 0, 0));
   };
   auto sstore = [&](int buf) {
     bf16_t* as = smem + buf * A_STAGE;
@@ -127,25 +144,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const int b_frag_krow = 8 * (grp >> 1) + (li >> 2);
   const int b_frag_col = wn * 128 + 16 * (grp & 1) + 4 * (li & 3);
 
-  auto compute = [&](int buf) {
-    const bf16_t* as = smem + buf * A_STAGE;
-    const bf16_t* bs = smem + 2 * A_STAGE + buf * B_STAGE;
+  // Fragments are double-buffered in registers: the LDS reads of sub-step ks+1 are issued
+  // before the 16 MFMAs of sub-step ks, so their latency hides behind the matrix work.
+  bf16x8_t fa[2][4], fb[2][4];
+  auto load_frags = [&](const bf16_t* as, const bf16_t* bs, int ks, int slot) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t af[4], bfr[4];
+    for (int i = 0; i < 4; ++i)
+      fa[slot][i] = *(const bf16x8_t*)(as + (a_frag_row + 32 * i) * A_PITCH + ks * 16 + a_frag_k);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const bf16x8_t*)(as + (a_frag_row + 32 * i) * A_PITCH + ks * 16 + a_frag_k);
+    for (int j = 0; j < 4; ++j)
+      fb[slot][j] = ds_read_tr_pair(bs + (ks * 16 + b_frag_krow) * B_PITCH + b_frag_col + 32 * j,
+                                    4 * B_PITCH);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = ds_read_tr_pair(bs + (ks * 16 + b_frag_krow) * B_PITCH + b_frag_col + 32 * j,
-                                 4 * B_PITCH);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
   };
 
   const int nk = (int)((K + BK - 1) / BK);
@@ -154,9 +170,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((int64_t)(kt + 1) * BK);
-    compute(cur);
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    const bool more = kt + 1 < nk;
+    const bf16_t* as = smem + cur * A_STAGE;
+    const bf16_t* bs = smem + 2 * A_STAGE + cur * B_STAGE;
+    // The scheduling fences keep this order; without them the compiler sinks each fragment
+    // read next to its first use and the LDS latency is exposed before every MFMA group.
+    if (more) gload((int64_t)(kt + 1) * BK);
+    load_frags(as, bs, 0, 0);
+    load_frags(as, bs, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(as, bs, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(as, bs, 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) sstore(cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(1);
     __syncthreads();
   }
 

@@ -11,6 +11,11 @@ using namespace tpk;
 namespace {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The GEMM tile addresses a 256-row panel of the activation operand and a 64-row panel of
+// the weight with 32-bit byte offsets, which bounds the two leading dimensions.
+constexpr int64_t MAX_LD_ACT = 1 << 21;
+constexpr int64_t MAX_LD_WEIGHT = 1 << 23;
 inline bool mult8(int64_t v) { return (v & 7) == 0; }
 
 inline int check_rank(int rank, int world) {
@@ -29,6 +34,7 @@ int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
   if (world < 1) return TP_ERR_RANK;
   if (batch <= 0 || seq <= 0 || H <= 0 || n_heads <= 0 || head_dim <= 0) return TP_ERR_SHAPE;
   if ((int64_t)n_heads * head_dim != H || head_dim != 128) return TP_ERR_SHAPE;
+  if (H > MAX_LD_ACT) return TP_ERR_SHAPE;
   if (n_heads % world) return TP_ERR_DIVISIBLE;
   s->T = batch * seq;
   s->hl = n_heads / world;
@@ -69,6 +75,7 @@ int tp_col_linear_gelu(const void* X, const void* W, void* Y, int64_t ldy, int64
   if (N % world) return TP_ERR_DIVISIBLE;
   const int64_t nl = N / world;
   if (ldy < nl) return TP_ERR_SHAPE;
+  if (H > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return TP_ERR_ALIGN;
   if (!mult8(H) || !mult8(N) || !mult8(nl) || !mult8(ldy)) return TP_ERR_ALIGN;
 
@@ -98,6 +105,7 @@ int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpar
   if (int st = check_rank(rank, world)) return st;
   if (seq <= 0 || K <= 0 || N <= 0) return TP_ERR_SHAPE;
   if (ldx < K) return TP_ERR_SHAPE;
+  if (ldx > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
   if (K % world) return TP_ERR_DIVISIBLE;
   const int64_t kl = K / world;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Zpart)) return TP_ERR_ALIGN;

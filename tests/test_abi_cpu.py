@@ -114,6 +114,8 @@ CASES = [
     ("col H % 8", col, dict(H=252), "TP_ERR_ALIGN"),
     ("col N/world % 8", col, dict(N=1028, world=2, ldy=1028), "TP_ERR_ALIGN"),
     ("col ldy % 8", col, dict(ldy=516), "TP_ERR_ALIGN"),
+    ("col H beyond 2^21", col, dict(H=(1 << 21) + 8), "TP_ERR_SHAPE"),
+    ("col N beyond 2^23", col, dict(N=(1 << 23) + 16, ldy=(1 << 22) + 8), "TP_ERR_SHAPE"),
     # row-parallel partial
     ("row null X", row, dict(X=None), "TP_ERR_NULL"),
     ("row null Z", row, dict(Z=None), "TP_ERR_NULL"),
@@ -125,6 +127,8 @@ CASES = [
     ("row K/world % 8", row, dict(K=1032, ldx=1032, world=2), "TP_ERR_ALIGN"),
     ("row misaligned W", row, dict(W=P + 4), "TP_ERR_ALIGN"),
     ("row ldx % 8", row, dict(ldx=1028), "TP_ERR_ALIGN"),
+    ("row ldx beyond 2^21", row, dict(ldx=(1 << 21) + 8), "TP_ERR_SHAPE"),
+    ("row N beyond 2^23", row, dict(N=(1 << 23) + 8), "TP_ERR_SHAPE"),
     # attention-head shard
     ("attn null Wo", attn, dict(Wo=None), "TP_ERR_NULL"),
     ("attn f32", attn, dict(dtype=0), "TP_ERR_DTYPE"),
@@ -132,6 +136,7 @@ CASES = [
     ("attn H != heads*d", attn, dict(H=1000), "TP_ERR_SHAPE"),
     ("attn head_dim 64", attn, dict(d=64, nh=16), "TP_ERR_SHAPE"),
     ("attn seq 0", attn, dict(seq=0), "TP_ERR_SHAPE"),
+    ("attn H beyond 2^21", attn, dict(H=(1 << 21) + 128 * 4, nh=(1 << 14) + 4), "TP_ERR_SHAPE"),
     ("attn heads % world", attn, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
     ("attn no workspace", attn, dict(ws=None), "TP_ERR_WORKSPACE"),
     ("attn small workspace", attn, dict(wsb=1000), "TP_ERR_WORKSPACE"),
