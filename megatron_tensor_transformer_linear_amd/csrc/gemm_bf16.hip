@@ -8,18 +8,29 @@
 // 1.1 and figure 1.2: the two block views of a matrix product that make the column and
 // outer-product-sum splits).
 //
-// Tile: 256 x 256 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave owning a 128 x 128
-// sub-tile as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
-// Operands are staged HBM -> registers -> LDS, double-buffered, one barrier per K step:
-//   - A tile [256][64] is K-contiguous, as the MFMA A operand wants (8 consecutive k per
-//     lane): one 16-byte LDS read per fragment.  Row pitch 72 elements keeps the 8 lanes of
-//     each 16-byte LDS phase on distinct banks.
-//   - B tile [64][256] keeps W's row-major layout (N-contiguous).  The MFMA B operand needs
-//     8 consecutive k per lane; the gfx950 LDS transpose read ds_read_b64_tr_b16 delivers
-//     exactly that: within each 16-lane group, lane 4q+c receives element c of the 8-byte
-//     rows addressed by lanes q, q+4, q+8, q+12.  Pointing lane (q + 4s) at row k0+s,
-//     columns n0+4q..4q+3 leaves lane i holding column n0+i, rows k0..k0+3; two reads give
-//     the 8 k values.  Row pitch 272 elements puts the 4 rows of a read on distinct banks.
+// Tile: 256 x BN x 32 per K step (BN = 256, 192 or 128), 256 threads = 4 waves in a 2 x 2
+// grid, each wave owning a 128 x BN/2 sub-tile as 4 x (BN/64) blocks of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators in AGPRs).
+//
+// Staging: HBM -> LDS directly (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at
+// LDS base + 16 * lane, no VGPR round trip), in a ring of 4 stages, so the loads of stage
+// kt + 4 are issued while stage kt is being multiplied, three K steps ahead of their use.
+// The data arrangement inside a stage is chosen by which global chunk each lane fetches:
+//   - A stage [256 rows][32 k] (64 B per row, K-contiguous as the MFMA A operand wants):
+//     row r keeps its four 16-byte k-chunks XOR-permuted by ((r >> 1) ^ (r >> 3)) & 3, so
+//     the 16-byte fragment reads of 16 consecutive rows fall on distinct bank groups.
+//   - B stage [32 k-rows][256 columns] (N-contiguous, W's own layout): k-row k keeps its
+//     16-byte column chunks XOR-permuted by 4 (k & 3) ^ 2 ((k >> 1) & 1), which puts the
+//     4 rows x 32 bytes of each transpose read on distinct banks.
+// The MFMA B operand needs 8 consecutive k per lane; the gfx950 LDS transpose read
+// ds_read_b64_tr_b16 delivers them from the N-contiguous tile: within each 16-lane group,
+// lane 4q+c receives element c of the 8-byte rows addressed by lanes q, q+4, q+8, q+12, so
+// pointing lane (q + 4s) at k-row k0+s, columns n0+4q..4q+3 leaves lane i holding column
+// n0+i, k-rows k0..k0+3; two reads give the 8 k values.
+// Per K step each wave issues its fragment reads for the second half-step under the
+// MFMAs of the first, waits for its own loads of the next stage, meets the other waves at
+// one barrier, queues the next stage's loads into the buffer just drained, and reads the
+// next stage's first fragments under the MFMAs of the second half-step.
 // Block -> tile mapping is XCD-aware: workgroups are dispatched round-robin over the 8 XCDs,
 // so consecutive logical tiles are given to the same XCD (shared L2), and logical tiles
 // walk 8-tile-row groups so an XCD's tiles share A and B panels.
@@ -28,25 +39,72 @@
 namespace tpk {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BK = 32, NST = 4;
 constexpr int NTHREADS = 256;
-constexpr int A_PITCH = BK + 8;   // elements (144 B)
-constexpr int B_PITCH = BN + 16;  // elements (544 B)
-constexpr int A_STAGE = BM * A_PITCH;
-constexpr int B_STAGE = BK * B_PITCH;
-constexpr int SMEM_ELEMS = 2 * A_STAGE + 2 * B_STAGE;  // 143360 bytes
+constexpr int A_BYTES = BM * BK * 2;  // one A stage: 16 KB
+constexpr uint32_t OOB = 0x80000000u; // buffer offset past every resource range
 
+typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8_t;
 
-__device__ __forceinline__ bf16x8_t ds_read_tr_pair(const bf16_t* p, int second_offset) {
-  const lds_bf16_t* lp = (const lds_bf16_t*)p;
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt[3:0] in
+// bits 3:0 and vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// vmcnt(N) and lgkmcnt(0) together.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads (those would wait
+// for every outstanding LDS-bound load); memory order is kept by the explicit waits.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Raw buffer resource: base address, no stride, `bytes` bytes in range (loads at offsets at
+// or past it return zeros), raw-buffer flags.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4_t r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)((a >> 32) & 0xFFFF);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+// One direct-to-LDS 16-byte load per lane: lane i's bytes land at LDS address
+// lds_addr + 16 i.  Issued through inline assembly so that the compiler does not order LDS
+// reads after it with a full vector-memory wait; completion is tracked by the explicit
+// vmcnt waits of the K loop.  M0 (the LDS base) is used by nothing else in the kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ bf16x8_t ds_read_tr_pair(const char* p, int second_offset) {
+  const lds_char_t* lp = (const lds_char_t*)p;
   i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lp);
   i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lp + second_offset));
   i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) ^ (2 * ((krow >> 1) & 1)); }
 
 __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& tile_m, int& tile_n) {
   const int nt = tm * tn;
@@ -63,14 +121,25 @@ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& tile_m
   tile_n = w / gsz;
 }
 
-template <int EPI>
+template <int BN, int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM_ELEMS];
+  constexpr int WN = BN / 2;                      // columns per wave
+  constexpr int NJ = WN / 32;                     // 32-wide MFMA blocks per wave
+  constexpr int BPITCH = BN == 128 ? 256 : 512;   // bytes per B k-row in LDS
+  constexpr int CPR = BPITCH / 16;                // 16-byte chunks per B k-row
+  constexpr int RPI = 1024 / BPITCH;              // B k-rows per wave load instruction
+  constexpr int B_BYTES = BK * BPITCH;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LD = A_BYTES / 1024 / 4;        // load instructions per wave per stage
+  constexpr int B_LD = B_BYTES / 1024 / 4;
+  constexpr int LPS = A_LD + B_LD;
+  static_assert(BN == 256 || BN == 192 || BN == 128, "tile width");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
 
   const int64_t M = g.M, N = g.N, K = g.K;
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
@@ -82,128 +151,138 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const bf16_t* __restrict__ B = (const bf16_t*)g.B;
   const int64_t lda = g.lda, ldb = g.ldb;
 
-  // Per-thread global coordinates of the staged chunks (16 bytes = 8 elements each).
-  const int a_row = tid >> 3, a_kc = (tid & 7) * 8;     // rows a_row + 32 i
-  const int b_row = tid >> 5, b_nc = (tid & 31) * 8;    // k-rows b_row + 8 i
-  const int64_t b_nlog = n0 + b_nc;
-  const bool b_nvalid = b_nlog < N;
-  const int64_t b_col = (b_nlog / g.b_blk) * g.b_blk_stride + (b_nlog % g.b_blk);
-
-  // Staging loads are raw buffer loads: the hardware returns zeros for any offset past the
-  // resource's byte range, so tile edges need neither branches nor selects.  A's resource
-  // covers the tile's rows (rows >= M fall outside it); B's resource is re-based at every K
-  // step and covers the remaining K rows of that step.  Chunks past K (for A) or past N (for
-  // B) are given an offset outside every range.
-  constexpr uint32_t OOB = 0x80000000u;
+  // ---- per-lane source offsets of the direct-to-LDS loads
+  // A: instruction i of wave wv fills rows 16 (4 wv + i) .. +15 of the stage, 4 lanes a row.
   const int64_t a_rows = min((int64_t)BM, M - m0);
-  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + m0 * lda), (short)0, (int)(a_rows * lda * 2), 0x00020000);
-  uint32_t a_off[8];
+  const i32x4_t rsrc_a = buffer_rsrc(A + m0 * lda, a_rows * lda * 2);
+  uint32_t a_off[A_LD];
+  int a_k[A_LD];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a_off[i] = (uint32_t)(((a_row + 32 * i) * lda + a_kc) * 2);
-  uint32_t b_off[8];
+  for (int i = 0; i < A_LD; ++i) {
+    const int row = 16 * (A_LD * wv + i) + (lane >> 2);
+    const int c = (lane & 3) ^ swz_a(row);
+    a_k[i] = 8 * c;
+    a_off[i] = (uint32_t)((row * lda + 8 * c) * 2);
+  }
+  // B: instruction i of wave wv fills k-rows RPI (B_LD wv + i) .. of the stage.
+  uint32_t b_off[B_LD];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    b_off[i] = b_nvalid ? (uint32_t)(((b_row + 8 * i) * ldb + b_col) * 2) : OOB;
+  for (int i = 0; i < B_LD; ++i) {
+    const int krow = RPI * (B_LD * wv + i) + lane / CPR;
+    const int j = (lane % CPR) ^ swz_b(krow);
+    const int64_t nlog = n0 + 8 * j;
+    const bool ok = 8 * j < BN && nlog < N;
+    const int64_t col = (nlog / g.b_blk) * g.b_blk_stride + (nlog % g.b_blk);
+    b_off[i] = ok ? (uint32_t)((krow * ldb + col) * 2) : OOB;
+  }
 
-  uint4 ra[8], rb[8];
-  auto gload = [&](int64_t k0) {
-    const bool a_kok = k0 + a_kc < K;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
+  auto issue_stage = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BK;
+    const uint32_t sb = lds0 + (kt & (NST - 1)) * STAGE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rsrc_a, a_kok ? a_off[i] + (uint32_t)(k0 * 2) : OOB, 0, 0));
+    for (int i = 0; i < A_LD; ++i) {
+      const uint32_t off = k0 + a_k[i] < K ? a_off[i] + (uint32_t)(k0 * 2) : OOB;
+      dma16(sb + (A_LD * wv + i) * 1024, off, rsrc_a);
+    }
     const int64_t k_rows = min((int64_t)BK, K - k0);
-    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + k0 * ldb), (short)0, (int)(k_rows * ldb * 2), 0x00020000);
+    const i32x4_t rsrc_b = buffer_rsrc(B + k0 * ldb, k_rows * ldb * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, b_off[i], 0, 0));
-  };
-  auto sstore = [&](int buf) {
-    bf16_t* as = smem + buf * A_STAGE;
-    bf16_t* bs = smem + 2 * A_STAGE + buf * B_STAGE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(uint4*)(as + (a_row + 32 * i) * A_PITCH + a_kc) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(uint4*)(bs + (b_row + 8 * i) * B_PITCH + b_nc) = rb[i];
+    for (int i = 0; i < B_LD; ++i) dma16(sb + A_BYTES + (B_LD * wv + i) * 1024, b_off[i], rsrc_b);
   };
 
-  f32x16_t acc[4][4];
+  // ---- per-lane LDS fragment offsets (bytes within a stage)
+  const int r32 = lane & 31, kh = lane >> 5;
+  int a_rd[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    a_rd[ks] = (wm * 128 + r32) * 64 + (((2 * ks + kh) ^ swz_a(r32)) * 16);
+  const int grp = lane >> 4, li = lane & 15, q = li & 3, s = li >> 2;
+  int b_rd[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int chunk = (wn * WN) / 8 + 4 * j + 2 * (grp & 1) + (q >> 1);
+    b_rd[j] = A_BYTES + (8 * (grp >> 1) + s) * BPITCH + ((chunk ^ swz_b(s)) * 16) + (q & 1) * 8;
+  }
+
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Lane-constant parts of the LDS fragment addresses.
-  const int a_frag_row = wm * 128 + (lane & 31);
-  const int a_frag_k = 8 * (lane >> 5);
-  const int grp = lane >> 4, li = lane & 15;
-  const int b_frag_krow = 8 * (grp >> 1) + (li >> 2);
-  const int b_frag_col = wn * 128 + 16 * (grp & 1) + 4 * (li & 3);
-
-  // Fragments are double-buffered in registers: the LDS reads of sub-step ks+1 are issued
-  // before the 16 MFMAs of sub-step ks, so their latency hides behind the matrix work.
-  bf16x8_t fa[2][4], fb[2][4];
-  auto load_frags = [&](const bf16_t* as, const bf16_t* bs, int ks, int slot) {
+  bf16x8_t fa[2][4], fb[2][NJ];
+  auto read_frags = [&](const char* sb, int ks, int slot) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[slot][i] = *(const bf16x8_t*)(as + (a_frag_row + 32 * i) * A_PITCH + ks * 16 + a_frag_k);
+    for (int i = 0; i < 4; ++i) fa[slot][i] = *(const bf16x8_t*)(sb + a_rd[ks] + i * 32 * 64);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[slot][j] = ds_read_tr_pair(bs + (ks * 16 + b_frag_krow) * B_PITCH + b_frag_col + 32 * j,
-                                    4 * B_PITCH);
+    for (int j = 0; j < NJ; ++j)
+      fb[slot][j] = ds_read_tr_pair(sb + b_rd[j] + ks * 16 * BPITCH, 4 * BPITCH);
   };
   auto mfmas = [&](int slot) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+  };
+  // Wait until this wave's loads of stage `need` have landed, given that the loads of
+  // every stage up to `issued` have been queued.
+  auto wait_stage = [&](int need, int issued, bool lgkm) {
+    const int later = issued - need;
+    if (lgkm) {
+      if (later >= 2) wait_vmcnt_lgkm0<2 * LPS>();
+      else if (later == 1) wait_vmcnt_lgkm0<LPS>();
+      else wait_vmcnt_lgkm0<0>();
+    } else {
+      if (later >= 2) wait_vmcnt<2 * LPS>();
+      else if (later == 1) wait_vmcnt<LPS>();
+      else wait_vmcnt<0>();
+    }
   };
 
   const int nk = (int)((K + BK - 1) / BK);
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  const int pro = min(NST, nk);
+  for (int kt = 0; kt < pro; ++kt) issue_stage(kt);
+  {
+    const int issued = pro - 1;
+    const int later = issued;  // stages queued after stage 0
+    if (later >= 3) wait_vmcnt<3 * LPS>();
+    else if (later == 2) wait_vmcnt<2 * LPS>();
+    else if (later == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+  }
+  lds_barrier();
+  read_frags(smem, 0, 0);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    const bf16_t* as = smem + cur * A_STAGE;
-    const bf16_t* bs = smem + 2 * A_STAGE + cur * B_STAGE;
-    // The scheduling fences keep this order; without them the compiler sinks each fragment
-    // read next to its first use and the LDS latency is exposed before every MFMA group.
-    if (more) gload((int64_t)(kt + 1) * BK);
-    load_frags(as, bs, 0, 0);
-    load_frags(as, bs, 1, 1);
+    const char* cur = smem + (kt & (NST - 1)) * STAGE;
+    read_frags(cur, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(0);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(as, bs, 2, 0);
+    // Stage kt+1 must have landed (every wave's share) and every wave must be done reading
+    // stage kt before its buffer is refilled with stage kt+4.
+    wait_stage(kt + 1, min(nk - 1, kt + NST - 1), true);
+    lds_barrier();
+    if (kt + NST < nk) issue_stage(kt + NST);
+    if (kt + 1 < nk) read_frags(smem + ((kt + 1) & (NST - 1)) * STAGE, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(1);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags(as, bs, 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) sstore(cur ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __syncthreads();
   }
 
   // Epilogue.  Accumulator element r of block (i, j) sits at
   //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,  col = 32 j + lane % 32
-  // of the wave's 128 x 128 sub-tile.
+  // of the wave's 128 x WN sub-tile.
   const int64_t ldc = g.ldc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = n0 + wn * WN + 32 * j + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -221,21 +300,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream) {
+template <int BN>
+hipError_t launch_bn(const GemmDesc& g, hipStream_t stream) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   const int64_t blocks = tm * tn;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(NTHREADS);
   switch (g.epi) {
-    case EPI_STORE: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_STORE>, grid, block, 0, stream, g); break;
-    case EPI_GELU_TANH: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_GELU_TANH>, grid, block, 0, stream, g); break;
-    case EPI_PARTIAL_F32: hipLaunchKernelGGL(gemm_bf16_kernel<EPI_PARTIAL_F32>, grid, block, 0, stream, g); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<BN, EPI_STORE>), grid, block, 0, stream, g); break;
+    case EPI_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<BN, EPI_GELU_TANH>), grid, block, 0, stream, g); break;
+    case EPI_PARTIAL_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BN, EPI_PARTIAL_F32>), grid, block, 0, stream, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile width per shape: the fewest rounds of workgroups over the 256 compute units, each
+// round costing its tile width, ties going to the wider tile.
+int gemm_bf16_tile_n(int64_t M, int64_t N) {
+  const int64_t tm = (M + BM - 1) / BM;
+  int best = 256;
+  int64_t best_cost = -1;
+  for (int bn : {256, 192, 128}) {
+    const int64_t tiles = tm * ((N + bn - 1) / bn);
+    const int64_t cost = ((tiles + 255) / 256) * bn;
+    if (best_cost < 0 || cost < best_cost) { best = bn; best_cost = cost; }
+  }
+  return best;
+}
+
+hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream) {
+  switch (gemm_bf16_tile_n(g.M, g.N)) {
+    case 192: return launch_bn<192>(g, stream);
+    case 128: return launch_bn<128>(g, stream);
+    default: return launch_bn<256>(g, stream);
+  }
 }
 
 }  // namespace tpk
