@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-inline-asm",
                 "-I" + INCLUDE] + DEVICE_FLAGS
 
 

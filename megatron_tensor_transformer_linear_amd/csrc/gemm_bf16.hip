@@ -34,6 +34,8 @@
 // Block -> tile mapping is XCD-aware: workgroups are dispatched round-robin over the 8 XCDs,
 // so consecutive logical tiles are given to the same XCD (shared L2), and logical tiles
 // walk 8-tile-row groups so an XCD's tiles share A and B panels.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tpk {
@@ -72,26 +74,29 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Raw buffer resource: base address, no stride, `bytes` bytes in range (loads at offsets at
-// or past it return zeros), raw-buffer flags.
+// or past it return zeros), raw-buffer flags.  The arguments are wave-uniform; the resource
+// is made to live in scalar registers.
 __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = (uint64_t)base;
   i32x4_t r;
-  r.x = (int)(uint32_t)a;
-  r.y = (int)((a >> 32) & 0xFFFF);
-  r.z = (int)bytes;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
   r.w = 0x00020000;
   return r;
 }
 
-// One direct-to-LDS 16-byte load per lane: lane i's bytes land at LDS address
-// lds_addr + 16 i.  Issued through inline assembly so that the compiler does not order LDS
-// reads after it with a full vector-memory wait; completion is tracked by the explicit
-// vmcnt waits of the K loop.  M0 (the LDS base) is used by nothing else in the kernel.
+// One direct-to-LDS 16-byte load per lane: lane i's 16 bytes, read from buffer offset
+// voff + soff, land at LDS address lds_base + IMM + 16 i.  Issued through inline assembly
+// so that the compiler does not order LDS reads after it with a full vector-memory wait;
+// completion is tracked by the explicit vmcnt waits of the K loop.  M0 (the LDS address of
+// the load) is set here and used by nothing else in the kernel.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, i32x4_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, i32x4_t rsrc, uint32_t soff) {
+  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds"
+               :: "s"(lds_base), "i"(IMM), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -101,6 +106,15 @@ __device__ __forceinline__ bf16x8_t ds_read_tr_pair(const char* p, int second_of
   i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lp + second_offset));
   i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}).
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 __device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
@@ -176,21 +190,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     b_off[i] = ok ? (uint32_t)((krow * ldb + col) * 2) : OOB;
   }
 
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
-  auto issue_stage = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
-    const uint32_t sb = lds0 + (kt & (NST - 1)) * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const uint32_t off = k0 + a_k[i] < K ? a_off[i] + (uint32_t)(k0 * 2) : OOB;
-      dma16(sb + (A_LD * wv + i) * 1024, off, rsrc_a);
-    }
-    const int64_t k_rows = min((int64_t)BK, K - k0);
-    const i32x4_t rsrc_b = buffer_rsrc(B + k0 * ldb, k_rows * ldb * 2);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) dma16(sb + A_BYTES + (B_LD * wv + i) * 1024, b_off[i], rsrc_b);
-  };
-
   // ---- per-lane LDS fragment offsets (bytes within a stage)
   const int r32 = lane & 31, kh = lane >> 5;
   int a_rd[2];
@@ -212,67 +211,107 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
   bf16x8_t fa[2][4], fb[2][NJ];
-  auto read_frags = [&](const char* sb, int ks, int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[slot][i] = *(const bf16x8_t*)(sb + a_rd[ks] + i * 32 * 64);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      fb[slot][j] = ds_read_tr_pair(sb + b_rd[j] + ks * 16 * BPITCH, 4 * BPITCH);
+
+  const int nk = (int)((K + BK - 1) / BK);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
+  const uint32_t lds_a = lds0 + (uint32_t)(wv * A_LD * 1024);            // this wave's A loads
+  const uint32_t lds_b = lds0 + (uint32_t)(A_BYTES + wv * B_LD * 1024);  // this wave's B loads
+
+  // ---- the work items a K step is made of
+  constexpr int NM = 4 * NJ;  // MFMAs per half-step
+  constexpr int NR = 4 + NJ;  // fragment-read items per half-step (a B item is two reads)
+  // MFMA m of a half-step: row block m / NJ, column block m % NJ.
+  auto mfma = [&](int slot, int m) {
+    const int i = m / NJ, j = m % NJ;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
   };
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-  };
-  // Wait until this wave's loads of stage `need` have landed, given that the loads of
-  // every stage up to `issued` have been queued.
-  auto wait_stage = [&](int need, int issued, bool lgkm) {
-    const int later = issued - need;
-    if (lgkm) {
-      if (later >= 2) wait_vmcnt_lgkm0<2 * LPS>();
-      else if (later == 1) wait_vmcnt_lgkm0<LPS>();
-      else wait_vmcnt_lgkm0<0>();
+  // Read item t of sub-step ks of the stage held in buffer `buf` into fragment slot `slot`.
+  auto read_item = [&](int buf, int ks, int slot, int t) {
+    const char* sb = smem + buf * STAGE;
+    if (t < 4) {
+      fa[slot][t] = *(const bf16x8_t*)(sb + a_rd[ks] + t * 32 * 64);
     } else {
-      if (later >= 2) wait_vmcnt<2 * LPS>();
-      else if (later == 1) wait_vmcnt<LPS>();
-      else wait_vmcnt<0>();
+      const int j = t - 4;
+      fb[slot][j] = ds_read_tr_pair(sb + b_rd[j] + ks * 16 * BPITCH, 4 * BPITCH);
+    }
+  };
+  // Load item U of stage kd into buffer BUF (U < A_LD: an A load, else a B load).  Parts of
+  // the stage past K, and whole stages past K, come back as zeros (out-of-range offsets or
+  // an empty B range), so the K loop can run whole groups of NST steps.  The B resource is
+  // re-based at every stage so that its range check alone bounds the rows read.
+  const int Ki = (int)K;                       // K < 2^31 (bounded by the leading dimensions)
+  const int ldb2 = (int)(ldb * 2);             // bytes per B row
+  const char* const Bbytes = (const char*)B;
+  auto dma_item = [&](auto BUFC, auto UC, int kd) {
+    constexpr int BUF = decltype(BUFC)::value, U = decltype(UC)::value;
+    const int k0 = kd * BK;
+    if constexpr (U < A_LD) {
+      const uint32_t off = a_k[U] < Ki - k0 ? a_off[U] : OOB;
+      dma16<BUF * STAGE + U * 1024>(lds_a, off, rsrc_a, (uint32_t)k0 * 2u);
+    } else {
+      constexpr int I = U - A_LD;
+      const int k_rows = max(0, min(BK, Ki - k0));
+      const i32x4_t rsrc_b = buffer_rsrc(Bbytes + (int64_t)k0 * ldb2, (int64_t)(k_rows * ldb2));
+      dma16<BUF * STAGE + I * 1024>(lds_b, b_off[I], rsrc_b, 0u);
     }
   };
 
-  const int nk = (int)((K + BK - 1) / BK);
-  const int pro = min(NST, nk);
-  for (int kt = 0; kt < pro; ++kt) issue_stage(kt);
-  {
-    const int issued = pro - 1;
-    const int later = issued;  // stages queued after stage 0
-    if (later >= 3) wait_vmcnt<3 * LPS>();
-    else if (later == 2) wait_vmcnt<2 * LPS>();
-    else if (later == 1) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
-  }
-  lds_barrier();
-  read_frags(smem, 0, 0);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = smem + (kt & (NST - 1)) * STAGE;
-    read_frags(cur, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(0);
-    __builtin_amdgcn_sched_barrier(0);
-    // Stage kt+1 must have landed (every wave's share) and every wave must be done reading
-    // stage kt before its buffer is refilled with stage kt+4.
-    wait_stage(kt + 1, min(nk - 1, kt + NST - 1), true);
+  // One K step on the stage in buffer S (kt % NST == S).  First half: the MFMAs of sub-step 0
+  // with the reads of sub-step 1 between them.  Then the wait for this wave's loads of stage
+  // kt+1 (two later stages may still be in flight) and the barrier, after which every wave's
+  // share of stage kt+1 has landed and buffer S is no longer read.  Second half: the MFMAs
+  // of sub-step 1 with the reads of stage kt+1's sub-step 0 and the loads of stage kt+NST
+  // into buffer S between them.  Each item is fenced in place, so the issue order is
+  // exactly this interleave.
+  auto step = [&](auto SC, int kt) {
+    constexpr int S = decltype(SC)::value;
+    static_for<NM>([&](auto MC) {
+      constexpr int m = decltype(MC)::value;
+      mfma(0, m);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (m < NR) read_item(S, 1, 1, m);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    wait_vmcnt_lgkm0<2 * LPS>();
     lds_barrier();
-    if (kt + NST < nk) issue_stage(kt + NST);
-    if (kt + 1 < nk) read_frags(smem + ((kt + 1) & (NST - 1)) * STAGE, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(1);
-    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NITEM = NR + LPS;
+    static_for<NM>([&](auto MC) {
+      constexpr int m = decltype(MC)::value;
+      mfma(1, m);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<NITEM>([&](auto TC) {
+        constexpr int t = decltype(TC)::value;
+        if constexpr (t * NM / NITEM == m) {
+          if constexpr (t < NR) read_item((S + 1) % NST, 0, 0, t);
+          else dma_item(SC, std::integral_constant<int, t - NR>{}, kt + NST);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- prologue: stages 0 .. NST-1 in flight, stage 0 landed, its first fragments read
+  static_for<NST>([&](auto SC) {
+    static_for<LPS>([&](auto UC) { dma_item(SC, UC, decltype(SC)::value); });
+  });
+  wait_vmcnt<(NST - 1) * LPS>();
+  lds_barrier();
+#pragma unroll
+  for (int t = 0; t < NR; ++t) read_item(0, 0, 0, t);
+
+  // ---- main loop over groups of NST steps (the last group may run on zero-filled stages)
+  const int ngroups = (nk + NST - 1) / NST;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const int kt = gi * NST;
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + 1);
+    step(std::integral_constant<int, 2>{}, kt + 2);
+    step(std::integral_constant<int, 3>{}, kt + 3);
   }
+  // Loads of the stages past the end are still in flight: let them land before the LDS is
+  // reused or released.
+  wait_vmcnt<0>();
 
   // Epilogue.  Accumulator element r of block (i, j) sits at
   //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,  col = 32 j + lane % 32
