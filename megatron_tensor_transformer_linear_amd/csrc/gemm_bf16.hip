@@ -17,8 +17,10 @@
 // kt + 4 are issued while stage kt is being multiplied, three K steps ahead of their use.
 // The data arrangement inside a stage is chosen by which global chunk each lane fetches:
 //   - A stage [256 rows][32 k] (64 B per row, K-contiguous as the MFMA A operand wants):
-//     row r keeps its four 16-byte k-chunks XOR-permuted by ((r >> 1) ^ (r >> 3)) & 3, so
-//     the 16-byte fragment reads of 16 consecutive rows fall on distinct bank groups.
+//     row r keeps its four 16-byte k-chunks XOR-permuted by (r >> 2) & 3.  The LDS serves a
+//     16-byte read 16 lanes at a time from 64 four-byte banks (measured with the bank-conflict
+//     counter: 16 consecutive lanes over 256 contiguous bytes run conflict-free), and this
+//     permutation gives the 16 rows of each such group distinct 16-byte bank groups.
 //   - B stage [32 k-rows][256 columns] (N-contiguous, W's own layout): k-row k keeps its
 //     16-byte column chunks XOR-permuted by 4 (k & 3) ^ 2 ((k >> 1) & 1), which puts the
 //     4 rows x 32 bytes of each transpose read on distinct banks.
@@ -41,7 +43,7 @@
 namespace tpk {
 namespace {
 
-constexpr int BM = 256, BK = 32, NST = 4;
+constexpr int BM = 256, BK = 32;
 constexpr int NTHREADS = 256;
 constexpr int A_BYTES = BM * BK * 2;  // one A stage: 16 KB
 constexpr uint32_t OOB = 0x80000000u; // buffer offset past every resource range
@@ -117,7 +119,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ int swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) ^ (2 * ((krow >> 1) & 1)); }
 
 __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& tile_m, int& tile_n) {
@@ -135,7 +137,7 @@ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& tile_m
   tile_n = w / gsz;
 }
 
-template <int BN, int EPI>
+template <int BN, int NST, int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   constexpr int WN = BN / 2;                      // columns per wave
   constexpr int NJ = WN / 32;                     // 32-wide MFMA blocks per wave
@@ -257,45 +259,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     }
   };
 
-  // One K step on the stage in buffer S (kt % NST == S).  First half: the MFMAs of sub-step 0
-  // with the reads of sub-step 1 between them.  Then the wait for this wave's loads of stage
-  // kt+1 (two later stages may still be in flight) and the barrier, after which every wave's
-  // share of stage kt+1 has landed and buffer S is no longer read.  Second half: the MFMAs
-  // of sub-step 1 with the reads of stage kt+1's sub-step 0 and the loads of stage kt+NST
-  // into buffer S between them.  Each item is fenced in place, so the issue order is
-  // exactly this interleave.
-  auto step = [&](auto SC, int kt) {
-    constexpr int S = decltype(SC)::value;
+  // One K step on the stage in buffer S (kt % NST == S).  First half: the MFMAs of sub-step 0,
+  // with the reads of sub-step 1 and the second half of stage kt+NST-1's loads (into buffer
+  // S-1, free since the previous step's barrier) between them.  Then the wait for this
+  // wave's loads of stage kt+1 (the NST-2 later stages may still be in flight) and the
+  // barrier, after which every wave's share of stage kt+1 has landed and buffer S is no
+  // longer read.  Second half: the MFMAs of sub-step 1, with the reads of stage kt+1's
+  // sub-step 0 and the first half of stage kt+NST's loads (into buffer S) between them.
+  // Splitting each stage's loads over two half-steps keeps the four waves' 1 KB loads from
+  // arriving at the address unit in one burst.  Each item is fenced in place, so the issue
+  // order is exactly this interleave.
+  constexpr int LH = LPS / 2;  // loads of a stage issued in the second half of a step
+  auto half_step = [&](auto SC, auto SLOTC, auto LOC, auto HIC, auto RBUFC, int ks_read,
+                       int read_slot, auto DBUFC, int kd) {
+    constexpr int SLOT = decltype(SLOTC)::value;
+    constexpr int LO = decltype(LOC)::value, HI = decltype(HIC)::value;  // load items [LO, HI)
+    constexpr int RBUF = decltype(RBUFC)::value;
+    constexpr int NITEM = NR + (HI - LO);
+    (void)SC;
     static_for<NM>([&](auto MC) {
       constexpr int m = decltype(MC)::value;
-      mfma(0, m);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (m < NR) read_item(S, 1, 1, m);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    wait_vmcnt_lgkm0<2 * LPS>();
-    lds_barrier();
-    constexpr int NITEM = NR + LPS;
-    static_for<NM>([&](auto MC) {
-      constexpr int m = decltype(MC)::value;
-      mfma(1, m);
+      mfma(SLOT, m);
       __builtin_amdgcn_sched_barrier(0);
       static_for<NITEM>([&](auto TC) {
         constexpr int t = decltype(TC)::value;
         if constexpr (t * NM / NITEM == m) {
-          if constexpr (t < NR) read_item((S + 1) % NST, 0, 0, t);
-          else dma_item(SC, std::integral_constant<int, t - NR>{}, kt + NST);
+          if constexpr (t < NR) read_item(RBUF, ks_read, read_slot, t);
+          else dma_item(DBUFC, std::integral_constant<int, LO + t - NR>{}, kd);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
+  auto step = [&](auto SC, int kt) {
+    constexpr int S = decltype(SC)::value;
+    half_step(SC, std::integral_constant<int, 0>{}, std::integral_constant<int, LH>{},
+              std::integral_constant<int, LPS>{}, SC, 1, 1,
+              std::integral_constant<int, (S + NST - 1) % NST>{}, kt + NST - 1);
+    wait_vmcnt_lgkm0<(NST - 2) * LPS>();
+    lds_barrier();
+    half_step(SC, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, LH>{}, std::integral_constant<int, (S + 1) % NST>{}, 0, 0,
+              SC, kt + NST);
+  };
 
-  // ---- prologue: stages 0 .. NST-1 in flight, stage 0 landed, its first fragments read
-  static_for<NST>([&](auto SC) {
+  // ---- prologue: stages 0 .. NST-2 in flight, the first half of stage NST-1 (its second
+  // half goes out in the first step), stage 0 landed, its first fragments read
+  static_for<NST - 1>([&](auto SC) {
     static_for<LPS>([&](auto UC) { dma_item(SC, UC, decltype(SC)::value); });
   });
-  wait_vmcnt<(NST - 1) * LPS>();
+  static_for<LH>([&](auto UC) {
+    dma_item(std::integral_constant<int, NST - 1>{}, UC, NST - 1);
+  });
+  wait_vmcnt<(NST - 2) * LPS + LH>();
   lds_barrier();
 #pragma unroll
   for (int t = 0; t < NR; ++t) read_item(0, 0, 0, t);
@@ -304,10 +320,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const int ngroups = (nk + NST - 1) / NST;
   for (int gi = 0; gi < ngroups; ++gi) {
     const int kt = gi * NST;
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    step(std::integral_constant<int, 2>{}, kt + 2);
-    step(std::integral_constant<int, 3>{}, kt + 3);
+    static_for<NST>([&](auto SC) { step(SC, kt + decltype(SC)::value); });
   }
   // Loads of the stages past the end are still in flight: let them land before the LDS is
   // reused or released.
@@ -339,7 +352,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   }
 }
 
-template <int BN>
+template <int BN, int NST>
 hipError_t launch_bn(const GemmDesc& g, hipStream_t stream) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   const int64_t blocks = tm * tn;
@@ -347,9 +360,9 @@ hipError_t launch_bn(const GemmDesc& g, hipStream_t stream) {
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(NTHREADS);
   switch (g.epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<BN, EPI_STORE>), grid, block, 0, stream, g); break;
-    case EPI_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<BN, EPI_GELU_TANH>), grid, block, 0, stream, g); break;
-    case EPI_PARTIAL_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BN, EPI_PARTIAL_F32>), grid, block, 0, stream, g); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_STORE>), grid, block, 0, stream, g); break;
+    case EPI_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_GELU_TANH>), grid, block, 0, stream, g); break;
+    case EPI_PARTIAL_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_PARTIAL_F32>), grid, block, 0, stream, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -373,9 +386,9 @@ int gemm_bf16_tile_n(int64_t M, int64_t N) {
 
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream) {
   switch (gemm_bf16_tile_n(g.M, g.N)) {
-    case 192: return launch_bn<192>(g, stream);
-    case 128: return launch_bn<128>(g, stream);
-    default: return launch_bn<256>(g, stream);
+    case 192: return launch_bn<192, 4>(g, stream);
+    case 128: return launch_bn<128, 4>(g, stream);
+    default: return launch_bn<256, 4>(g, stream);
   }
 }
 
