@@ -119,6 +119,16 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// GeLU, tanh form, as x / (1 + exp(-2u)) with the hardware exp2 and reciprocal (the result
+// is rounded to bf16, far coarser than either approximation).
+__device__ __forceinline__ float gelu_tanh_fast(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float k1 = 0.044715f;
+  const float m2log2e = -2.0f * 1.4426950408889634f;
+  const float u = k0 * (x + k1 * x * x * x);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+}
+
 __device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz_b(int krow) { return (4 * (krow & 3)) ^ (2 * ((krow >> 1) & 1)); }
 
@@ -159,38 +169,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
 
   const int64_t M = g.M, N = g.N, K = g.K;
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  int tile_m, tile_n;
-  tile_coords(blockIdx.x, tm, tn, tile_m, tile_n);
-  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int nt = tm * tn;
+  const int nk = (int)((K + BK - 1) / BK);
+  const int ng = (nk + NST - 1) / NST;  // groups of NST K steps per tile (last one padded)
 
   const bf16_t* __restrict__ A = (const bf16_t*)g.A;
   const bf16_t* __restrict__ B = (const bf16_t*)g.B;
   const int64_t lda = g.lda, ldb = g.ldb;
 
-  // ---- per-lane source offsets of the direct-to-LDS loads
-  // A: instruction i of wave wv fills rows 16 (4 wv + i) .. +15 of the stage, 4 lanes a row.
-  const int64_t a_rows = min((int64_t)BM, M - m0);
-  const i32x4_t rsrc_a = buffer_rsrc(A + m0 * lda, a_rows * lda * 2);
-  uint32_t a_off[A_LD];
-  int a_k[A_LD];
+  // ---- per-lane source offsets of one tile's direct-to-LDS loads
+  // A: instruction i of wave wv fills rows 16 (A_LD wv + i) .. +15 of the stage, 4 lanes a
+  // row.  B: instruction i fills k-rows RPI (B_LD wv + i) .. of the stage.  A tile index past
+  // the end gets an empty A range and out-of-range B offsets: its stages load as zeros.
+  struct TileLoads {
+    i32x4_t rsrc_a;
+    uint32_t a_off[A_LD];
+    int a_k[A_LD];
+    uint32_t b_off[B_LD];
+  };
+  auto tile_loads = [&](int t, TileLoads& d) {
+    int tile_m = 0, tile_n = 0;
+    const bool live = t < nt;
+    if (live) tile_coords(t, tm, tn, tile_m, tile_n);
+    const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+    const int64_t a_rows = live ? min((int64_t)BM, M - m0) : 0;
+    d.rsrc_a = buffer_rsrc(A + m0 * lda, a_rows * lda * 2);
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int row = 16 * (A_LD * wv + i) + (lane >> 2);
-    const int c = (lane & 3) ^ swz_a(row);
-    a_k[i] = 8 * c;
-    a_off[i] = (uint32_t)((row * lda + 8 * c) * 2);
-  }
-  // B: instruction i of wave wv fills k-rows RPI (B_LD wv + i) .. of the stage.
-  uint32_t b_off[B_LD];
+    for (int i = 0; i < A_LD; ++i) {
+      const int row = 16 * (A_LD * wv + i) + (lane >> 2);
+      const int c = (lane & 3) ^ swz_a(row);
+      d.a_k[i] = 8 * c;
+      d.a_off[i] = (uint32_t)((row * lda + 8 * c) * 2);
+    }
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int krow = RPI * (B_LD * wv + i) + lane / CPR;
-    const int j = (lane % CPR) ^ swz_b(krow);
-    const int64_t nlog = n0 + 8 * j;
-    const bool ok = 8 * j < BN && nlog < N;
-    const int64_t col = (nlog / g.b_blk) * g.b_blk_stride + (nlog % g.b_blk);
-    b_off[i] = ok ? (uint32_t)((krow * ldb + col) * 2) : OOB;
-  }
+    for (int i = 0; i < B_LD; ++i) {
+      const int krow = RPI * (B_LD * wv + i) + lane / CPR;
+      const int j = (lane % CPR) ^ swz_b(krow);
+      const int64_t nlog = n0 + 8 * j;
+      const bool ok = live && 8 * j < BN && nlog < N;
+      const int64_t col = (nlog / g.b_blk) * g.b_blk_stride + (nlog % g.b_blk);
+      d.b_off[i] = ok ? (uint32_t)((krow * ldb + col) * 2) : OOB;
+    }
+  };
 
   // ---- per-lane LDS fragment offsets (bytes within a stage)
   const int r32 = lane & 31, kh = lane >> 5;
@@ -206,16 +226,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     b_rd[j] = A_BYTES + (8 * (grp >> 1) + s) * BPITCH + ((chunk ^ swz_b(s)) * 16) + (q & 1) * 8;
   }
 
+  // Accumulators of the wave's 128 x WN sub-tile, as 4 x NJ blocks of 32 x 32.
+  //   bf16 outputs (TRANS): each MFMA takes the W fragment as its first operand and the X
+  //     fragment as its second, so the block it accumulates is the transpose of the output
+  //     block: lane l's 16 values of block (i, j) are output row 32 i + l % 32, columns
+  //     32 j + 8 q + 4 (l / 32) + 0..3 for q = 0..3, stored 8 bytes (4 bf16) at a time.
+  //   fp32 outputs: X first, W second; lane l's value r of block (i, j) is output row
+  //     32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column 32 j + l % 32, so one 4-byte store per
+  //     value writes two whole 128-byte rows per instruction.
+  constexpr bool TRANS = EPI != EPI_PARTIAL_F32;
   f32x16_t acc[4][NJ];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  };
+  zero_acc();
   bf16x8_t fa[2][4], fb[2][NJ];
 
-  const int nk = (int)((K + BK - 1) / BK);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
   const uint32_t lds_a = lds0 + (uint32_t)(wv * A_LD * 1024);            // this wave's A loads
   const uint32_t lds_b = lds0 + (uint32_t)(A_BYTES + wv * B_LD * 1024);  // this wave's B loads
@@ -226,7 +257,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   // MFMA m of a half-step: row block m / NJ, column block m % NJ.
   auto mfma = [&](int slot, int m) {
     const int i = m / NJ, j = m % NJ;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+    if constexpr (TRANS)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[slot][j], fa[slot][i], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
   };
   // Read item t of sub-step ks of the stage held in buffer `buf` into fragment slot `slot`.
   auto read_item = [&](int buf, int ks, int slot, int t) {
@@ -238,45 +272,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       fb[slot][j] = ds_read_tr_pair(sb + b_rd[j] + ks * 16 * BPITCH, 4 * BPITCH);
     }
   };
-  // Load item U of stage kd into buffer BUF (U < A_LD: an A load, else a B load).  Parts of
-  // the stage past K, and whole stages past K, come back as zeros (out-of-range offsets or
-  // an empty B range), so the K loop can run whole groups of NST steps.  The B resource is
-  // re-based at every stage so that its range check alone bounds the rows read.
+  // Load item U of stage kd (counted within the tile whose loads `d` describes) into buffer
+  // BUF (U < A_LD: an A load, else a B load).  Parts of a stage past K, and whole stages
+  // past K, come back as zeros (out-of-range offsets or an empty B range), so the K loop
+  // can run whole groups of NST steps.  The B resource is re-based at every stage so that
+  // its range check alone bounds the rows read.
   const int Ki = (int)K;                       // K < 2^31 (bounded by the leading dimensions)
   const int ldb2 = (int)(ldb * 2);             // bytes per B row
   const char* const Bbytes = (const char*)B;
-  auto dma_item = [&](auto BUFC, auto UC, int kd) {
+  auto dma_item = [&](auto BUFC, auto UC, const TileLoads& d, int kd) {
     constexpr int BUF = decltype(BUFC)::value, U = decltype(UC)::value;
     const int k0 = kd * BK;
     if constexpr (U < A_LD) {
-      const uint32_t off = a_k[U] < Ki - k0 ? a_off[U] : OOB;
-      dma16<BUF * STAGE + U * 1024>(lds_a, off, rsrc_a, (uint32_t)k0 * 2u);
+      const uint32_t off = d.a_k[U] < Ki - k0 ? d.a_off[U] : OOB;
+      dma16<BUF * STAGE + U * 1024>(lds_a, off, d.rsrc_a, (uint32_t)k0 * 2u);
     } else {
       constexpr int I = U - A_LD;
       const int k_rows = max(0, min(BK, Ki - k0));
       const i32x4_t rsrc_b = buffer_rsrc(Bbytes + (int64_t)k0 * ldb2, (int64_t)(k_rows * ldb2));
-      dma16<BUF * STAGE + I * 1024>(lds_b, b_off[I], rsrc_b, 0u);
+      dma16<BUF * STAGE + I * 1024>(lds_b, d.b_off[I], rsrc_b, 0u);
     }
   };
 
-  // One K step on the stage in buffer S (kt % NST == S).  First half: the MFMAs of sub-step 0,
-  // with the reads of sub-step 1 and the second half of stage kt+NST-1's loads (into buffer
-  // S-1, free since the previous step's barrier) between them.  Then the wait for this
-  // wave's loads of stage kt+1 (the NST-2 later stages may still be in flight) and the
-  // barrier, after which every wave's share of stage kt+1 has landed and buffer S is no
-  // longer read.  Second half: the MFMAs of sub-step 1, with the reads of stage kt+1's
-  // sub-step 0 and the first half of stage kt+NST's loads (into buffer S) between them.
-  // Splitting each stage's loads over two half-steps keeps the four waves' 1 KB loads from
-  // arriving at the address unit in one burst.  Each item is fenced in place, so the issue
-  // order is exactly this interleave.
-  constexpr int LH = LPS / 2;  // loads of a stage issued in the second half of a step
-  auto half_step = [&](auto SC, auto SLOTC, auto LOC, auto HIC, auto RBUFC, int ks_read,
-                       int read_slot, auto DBUFC, int kd) {
+  // One half-step: the NM MFMAs on fragment slot SLOT, with NR fragment reads (sub-step
+  // ks_read of buffer RBUF into slot read_slot) and the load items [LO, HI) of stage kd
+  // (into buffer DBUF) spread between them, each item fenced in place.
+  auto half_step = [&](auto SLOTC, auto LOC, auto HIC, auto RBUFC, int ks_read, int read_slot,
+                       auto DBUFC, const TileLoads& d, int kd) {
     constexpr int SLOT = decltype(SLOTC)::value;
-    constexpr int LO = decltype(LOC)::value, HI = decltype(HIC)::value;  // load items [LO, HI)
+    constexpr int LO = decltype(LOC)::value, HI = decltype(HIC)::value;
     constexpr int RBUF = decltype(RBUFC)::value;
     constexpr int NITEM = NR + (HI - LO);
-    (void)SC;
     static_for<NM>([&](auto MC) {
       constexpr int m = decltype(MC)::value;
       mfma(SLOT, m);
@@ -285,79 +311,144 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         constexpr int t = decltype(TC)::value;
         if constexpr (t * NM / NITEM == m) {
           if constexpr (t < NR) read_item(RBUF, ks_read, read_slot, t);
-          else dma_item(DBUFC, std::integral_constant<int, LO + t - NR>{}, kd);
+          else dma_item(DBUFC, std::integral_constant<int, LO + t - NR>{}, d, kd);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto step = [&](auto SC, int kt) {
+  // One K step on the stage in buffer S.  First half: the MFMAs of sub-step 0, with the
+  // reads of sub-step 1 and the second half of the loads of the stage NST-1 ahead (into
+  // buffer S-1, free since the previous step's barrier) between them.  Then the wait for
+  // this wave's loads of the next stage (the NST-2 stages after it may still be in flight)
+  // and the barrier, after which every wave's share of the next stage has landed and buffer
+  // S is no longer read.  Second half: the MFMAs of sub-step 1, with the reads of the next
+  // stage's sub-step 0 and the first half of the loads of the stage NST ahead (into buffer
+  // S) between them.  Splitting each stage's loads over two half-steps keeps the four waves'
+  // 1 KB loads from reaching the address unit in one burst.
+  constexpr int LH = LPS / 2;
+  auto step = [&](auto SC, const TileLoads& d1, int kd1, const TileLoads& d2, int kd2) {
     constexpr int S = decltype(SC)::value;
-    half_step(SC, std::integral_constant<int, 0>{}, std::integral_constant<int, LH>{},
+    half_step(std::integral_constant<int, 0>{}, std::integral_constant<int, LH>{},
               std::integral_constant<int, LPS>{}, SC, 1, 1,
-              std::integral_constant<int, (S + NST - 1) % NST>{}, kt + NST - 1);
+              std::integral_constant<int, (S + NST - 1) % NST>{}, d1, kd1);
     wait_vmcnt_lgkm0<(NST - 2) * LPS>();
     lds_barrier();
-    half_step(SC, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
-              std::integral_constant<int, LH>{}, std::integral_constant<int, (S + 1) % NST>{}, 0, 0,
-              SC, kt + NST);
+    half_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+              std::integral_constant<int, LH>{}, std::integral_constant<int, (S + 1) % NST>{},
+              0, 0, SC, d2, kd2);
   };
 
-  // ---- prologue: stages 0 .. NST-2 in flight, the first half of stage NST-1 (its second
+  // ---- persistent loop over this workgroup's tiles t = blockIdx.x + i * gridDim.x.  The
+  // stage stream runs on across tiles: the last group of K steps of a tile loads the first
+  // stages of the next one, so the loads are in flight during the epilogue.
+  TileLoads cur, nxt;
+  int t = blockIdx.x;
+  tile_loads(t, cur);
+  // prologue: stages 0 .. NST-2 and the first half of stage NST-1 in flight (its second
   // half goes out in the first step), stage 0 landed, its first fragments read
   static_for<NST - 1>([&](auto SC) {
-    static_for<LPS>([&](auto UC) { dma_item(SC, UC, decltype(SC)::value); });
+    static_for<LPS>([&](auto UC) { dma_item(SC, UC, cur, decltype(SC)::value); });
   });
-  static_for<LH>([&](auto UC) {
-    dma_item(std::integral_constant<int, NST - 1>{}, UC, NST - 1);
-  });
+  static_for<LH>([&](auto UC) { dma_item(std::integral_constant<int, NST - 1>{}, UC, cur, NST - 1); });
   wait_vmcnt<(NST - 2) * LPS + LH>();
   lds_barrier();
 #pragma unroll
-  for (int t = 0; t < NR; ++t) read_item(0, 0, 0, t);
+  for (int r = 0; r < NR; ++r) read_item(0, 0, 0, r);
 
-  // ---- main loop over groups of NST steps (the last group may run on zero-filled stages)
-  const int ngroups = (nk + NST - 1) / NST;
-  for (int gi = 0; gi < ngroups; ++gi) {
-    const int kt = gi * NST;
-    static_for<NST>([&](auto SC) { step(SC, kt + decltype(SC)::value); });
-  }
-  // Loads of the stages past the end are still in flight: let them land before the LDS is
-  // reused or released.
-  wait_vmcnt<0>();
-
-  // Epilogue.  Accumulator element r of block (i, j) sits at
-  //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,  col = 32 j + lane % 32
-  // of the wave's 128 x WN sub-tile.
   const int64_t ldc = g.ldc;
+  for (; t < nt; t += gridDim.x) {
+    tile_loads(t + gridDim.x, nxt);
+    for (int gi = 0; gi < ng - 1; ++gi) {
+      const int kt = gi * NST;
+      static_for<NST>([&](auto SC) {
+        constexpr int S = decltype(SC)::value;
+        step(SC, cur, kt + S + NST - 1, cur, kt + S + NST);
+      });
+    }
+    {  // last group: from its first second half on, the loads are the next tile's
+      const int kt = (ng - 1) * NST;
+      step(std::integral_constant<int, 0>{}, cur, kt + NST - 1, nxt, 0);
+      static_for<NST - 1>([&](auto SC) {
+        constexpr int S = decltype(SC)::value + 1;
+        step(std::integral_constant<int, S>{}, nxt, S - 1, nxt, S);
+      });
+    }
+
+    // Epilogue of tile t (see the accumulator layout above).
+    int tile_m, tile_n;
+    tile_coords(t, tm, tn, tile_m, tile_n);
+    const int64_t m_w = (int64_t)tile_m * BM + wm * 128, n_w = (int64_t)tile_n * BN + wn * WN;
+    if constexpr (TRANS) {
+      const int64_t row0 = m_w + (lane & 31), col0 = n_w + 4 * (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = row0 + 32 * i;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t col = n0 + wn * WN + 32 * j + (lane & 31);
-      if (col >= N) continue;
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= M) continue;
-        float v = acc[i][j][r];
-        if (EPI == EPI_PARTIAL_F32) {
-          ((float*)g.C)[row * ldc + col] = v;
-        } else {
-          if (EPI == EPI_GELU_TANH) v = gelu_tanh_f32(v);
-          ((bf16_t*)g.C)[row * ldc + col] = f32_to_bf16(v);
+          for (int qq = 0; qq < 4; ++qq) {
+            const int64_t col = col0 + 32 * j + 8 * qq;
+            if (row < M && col < N) {
+              float v0 = acc[i][j][4 * qq], v1 = acc[i][j][4 * qq + 1];
+              float v2 = acc[i][j][4 * qq + 2], v3 = acc[i][j][4 * qq + 3];
+              if constexpr (EPI == EPI_GELU_TANH) {
+                v0 = gelu_tanh_fast(v0); v1 = gelu_tanh_fast(v1);
+                v2 = gelu_tanh_fast(v2); v3 = gelu_tanh_fast(v3);
+              }
+              uint2 u;
+              u.x = pack_bf16x2(v0, v1);
+              u.y = pack_bf16x2(v2, v3);
+              *(uint2*)((bf16_t*)g.C + row * ldc + col) = u;
+            }
+          }
+        }
+      }
+    } else {
+      const int64_t row0 = m_w + 4 * (lane >> 5), col0 = n_w + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int64_t col = col0 + 32 * j;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
+            if (row < M && col < N) ((float*)g.C)[row * ldc + col] = acc[i][j][r];
+          }
         }
       }
     }
+    zero_acc();
+    cur = nxt;
   }
+  // Loads of the stages past the last tile are still in flight: let them land before the
+  // workgroup's LDS is released.
+  wait_vmcnt<0>();
+}
+
+// Compute units of the current device (the persistent grid size), cached per device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <int BN, int NST>
 hipError_t launch_bn(const GemmDesc& g, hipStream_t stream) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
-  const int64_t blocks = tm * tn;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t tiles = tm * tn;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  // One workgroup per compute unit (each holds 128-160 KB of LDS), looping over tiles.
+  const int64_t blocks = min(tiles, (int64_t)device_cus());
   dim3 grid((unsigned)blocks), block(NTHREADS);
   switch (g.epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_STORE>), grid, block, 0, stream, g); break;
