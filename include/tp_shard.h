@@ -80,16 +80,20 @@ int tp_col_linear_gelu(const void* X, const void* W, void* Y, int64_t ldy,
 
 /* Row-parallel linear, partial sum of one rank (the all-reduce form, before the reduce).
  *
- *   Zpart[t, n] = sum_{k < K/world} X[t, rank*K/world + k] * W[rank*K/world + k, n]
+ *   Zpart[t, n] = sum_{k < K/world} X[t, k] * W[rank*K/world + k, n]
  *
- * X [seq, K] with leading dimension ldx >= K is the full input; its column block `rank` is
- * the rank's input shard (for the MLP this is exactly the column block the column-parallel
- * call wrote, e.g. Yfull with ldx = K).  W [K, N] dense (ld N); rank `rank` uses its row
- * block [rank*K/world, (rank+1)*K/world) (typc.net section 2.2; 0539edu.com section 1.1
+ * X is the rank's input shard x_partial [seq, K/world] with leading dimension
+ * ldx >= K/world: the row-parallel layer takes the partial input, not the full one
+ * (pwwt.cn section 3.3, RowParallelLinear.forward(x_partial)).  For the MLP this is exactly
+ * the block the rank's column-parallel call wrote, which stays on the rank (the column ->
+ * row pairing needs no exchange in between; 0539edu.com section 1.2.1).  If the input is
+ * held as one concatenated [seq, K] buffer, pass X = Xfull + rank*K/world and ldx = K.
+ * W [K, N] dense (ld N) is the full weight; rank `rank` uses its row block
+ * [rank*K/world, (rank+1)*K/world) (typc.net section 2.2; 0539edu.com section 1.1
  * formula 1.1 "outer-product-sum split"; pwwt.cn sections 1.2 and 3.3).  Zpart [seq, N] is
  * dense fp32 whatever the io dtype; the full result is the sum of all ranks' partials.
- * Errors: TP_ERR_NULL, TP_ERR_SHAPE (ldx < K), TP_ERR_DIVISIBLE (K % world), TP_ERR_RANK,
- * TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_LAUNCH. */
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE (ldx < K/world), TP_ERR_DIVISIBLE (K % world),
+ * TP_ERR_RANK, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_LAUNCH. */
 int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpart,
                           int64_t seq, int64_t K, int64_t N, int rank, int world,
                           int dtype, void* stream);

@@ -104,16 +104,16 @@ int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpar
   if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
   if (int st = check_rank(rank, world)) return st;
   if (seq <= 0 || K <= 0 || N <= 0) return TP_ERR_SHAPE;
-  if (ldx < K) return TP_ERR_SHAPE;
-  if (ldx > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
   if (K % world) return TP_ERR_DIVISIBLE;
   const int64_t kl = K / world;
+  if (ldx < kl) return TP_ERR_SHAPE;
+  if (ldx > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(W) || !aligned16(Zpart)) return TP_ERR_ALIGN;
   if (!mult8(ldx) || !mult8(kl) || !mult8(N)) return TP_ERR_ALIGN;
 
   const size_t es = dtype == TP_BF16 ? 2 : 4;
   GemmDesc g;
-  g.A = (const char*)X + (size_t)rank * kl * es;       // column block `rank` of X[seq, K]
+  g.A = X;                                             // the rank's input shard [seq, K/world]
   g.lda = ldx;
   g.B = (const char*)W + (size_t)rank * kl * N * es;   // row block `rank` of W[K, N]
   g.ldb = N;

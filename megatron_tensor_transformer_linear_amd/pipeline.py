@@ -11,7 +11,8 @@ order the tensor-parallel layer runs them, one rank after another on one stream:
   * the attention-head shard (0539edu.com section 1.2.2; pwwt.cn section 2.2): per rank,
     QKV column split, the rank's heads, O row split to an fp32 partial;
   * the block (pwwt.cn section 2.1, figure 3): LayerNorm, attention shard of every rank,
-    reduce + residual + LayerNorm, MLP shard of every rank, reduce + residual.
+    reduce + residual + LayerNorm, MLP shard of every rank, reduce + residual.  Here each
+    rank's hidden activation is its own dense [T, F/P] buffer, as on separate GPUs.
 
 torch provides device memory and the stream only; all arithmetic is in the HIP kernels.
 """
@@ -73,8 +74,9 @@ class MLPShard:
                               self.F, r, self.P, tp.TP_ACT_GELU_TANH, self.dt, self.stream)
 
     def row(self, r: int):
-        tp.tp_row_linear_partial(self.Yfull, self.F, self.B, self.parts[r], self.T, self.F,
-                                 self.H, r, self.P, self.dt, self.stream)
+        fl = self.F // self.P
+        tp.tp_row_linear_partial(self.Yfull[:, r * fl:], self.F, self.B, self.parts[r], self.T,
+                                 self.F, self.H, r, self.P, self.dt, self.stream)
 
     def reduce(self):
         n = self.T * self.H
@@ -118,8 +120,9 @@ class LinearShard:
                               act, self.dt, self.stream)
 
     def row(self, r: int):
-        tp.tp_row_linear_partial(self.X, self.H, self.W, self.parts[r], self.T, self.H, self.N, r,
-                                 self.P, self.dt, self.stream)
+        kl = self.H // self.P
+        tp.tp_row_linear_partial(self.X[:, r * kl:], self.H, self.W, self.parts[r], self.T,
+                                 self.H, self.N, r, self.P, self.dt, self.stream)
 
     def reduce(self):
         tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.N, None, None, None,
@@ -194,7 +197,9 @@ class BlockShard:
         self.h = torch.empty_like(self.xn)
         self.hn = torch.empty_like(self.xn)
         self.out = torch.empty_like(self.xn)
-        self.Yfull = torch.empty(self.T, self.F, dtype=bf, device=dev)
+        # The hidden activation stays with its rank: Yr[r] = GeLU(hn . W1_r), dense
+        # [T, F/P], is the row call's input shard (no gather between the two MLP GEMMs).
+        self.Yr = torch.empty(world, self.T, self.F // world, dtype=bf, device=dev)
         self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
         self.ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, self.H, n_heads, head_dim, world,
                                                    tp.TP_BF16)
@@ -218,12 +223,13 @@ class BlockShard:
 
     def mlp_col(self, r: int):
         fl = self.F // self.P
-        tp.tp_col_linear_gelu(self.hn, self.W1, self.Yfull[:, r * fl:], self.F, self.T, self.H,
-                              self.F, r, self.P, tp.TP_ACT_GELU_TANH, tp.TP_BF16, self.stream)
+        tp.tp_col_linear_gelu(self.hn, self.W1, self.Yr[r], fl, self.T, self.H, self.F, r,
+                              self.P, tp.TP_ACT_GELU_TANH, tp.TP_BF16, self.stream)
 
     def mlp_row(self, r: int):
-        tp.tp_row_linear_partial(self.Yfull, self.F, self.W2, self.parts[r], self.T, self.F,
-                                 self.H, r, self.P, tp.TP_BF16, self.stream)
+        fl = self.F // self.P
+        tp.tp_row_linear_partial(self.Yr[r], fl, self.W2, self.parts[r], self.T, self.F, self.H,
+                                 r, self.P, tp.TP_BF16, self.stream)
 
     def reduce2(self):
         tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.h, None, None,

@@ -122,7 +122,7 @@ CASES = [
     ("row bad dtype", row, dict(dtype=2), "TP_ERR_DTYPE"),
     ("row rank > world", row, dict(rank=5), "TP_ERR_RANK"),
     ("row K 0", row, dict(K=0), "TP_ERR_SHAPE"),
-    ("row ldx < K", row, dict(ldx=1016), "TP_ERR_SHAPE"),
+    ("row ldx < K/world", row, dict(ldx=504), "TP_ERR_SHAPE"),
     ("row K % world", row, dict(K=1024, world=3, rank=0), "TP_ERR_DIVISIBLE"),
     ("row K/world % 8", row, dict(K=1032, ldx=1032, world=2), "TP_ERR_ALIGN"),
     ("row misaligned W", row, dict(W=P + 4), "TP_ERR_ALIGN"),

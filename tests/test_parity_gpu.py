@@ -307,10 +307,32 @@ def test_row_edge_shapes(lib, dtype, T, K, N, world, rank):
     Xv, Wv = host(Xd), host(Wd)
     Z = torch.empty(T, N, dtype=torch.float32, device=Xd.device)
     say(f"  row edge dtype={dtype} T={T} K={K} N={N} world={world} rank={rank}")
-    tp.tp_row_linear_partial(Xd, K + 16, Wd, Z, T, K, N, rank, world,
+    kl = K // world
+    tp.tp_row_linear_partial(Xd[:, rank * kl:], K + 16, Wd, Z, T, K, N, rank, world,
                              tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
     _sync()
     check("row partial", Z, O.row_linear_partial(Xv[:, :K], Wv, rank, world), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,K,N,world,rank", [(70, 1024, 264, 4, 3), (300, 6144, 136, 8, 2)])
+def test_row_dense_shard(lib, dtype, T, K, N, world, rank):
+    """The rank's input shard held as its own dense [T, K/world] buffer (ldx = K/world), as
+    the block keeps each rank's hidden activation."""
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(T * 7 + K + rank))
+    kl = K // world
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    W = (rng.standard_normal((K, N)) / np.sqrt(K)).astype(np.float32)
+    Xd, Wd = dev_values(X, dtype), dev_values(W, dtype)
+    Xv, Wv = host(Xd), host(Wd)
+    Xr = Xd[:, rank * kl:(rank + 1) * kl].contiguous()
+    Z = torch.empty(T, N, dtype=torch.float32, device=Xd.device)
+    say(f"  row dense shard dtype={dtype} T={T} K={K} N={N} world={world} rank={rank}")
+    tp.tp_row_linear_partial(Xr, kl, Wd, Z, T, K, N, rank, world,
+                             tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    check("row partial (dense shard)", Z, O.row_linear_partial(Xv, Wv, rank, world), dtype)
 
 
 @pytest.mark.parametrize("batch,seq,n_heads,world,causal", [
