@@ -5,10 +5,16 @@
 //
 //   h = residual + sum_{p ascending} parts[p];  y = (h - mean) / sqrt(var + eps) * gamma + beta
 //
-// HBM-bound: one workgroup per row streams every partial once (16-byte loads, coalesced
-// along the row), keeps the row in registers, and writes h and y once.  Row statistics are
-// a wave reduction (cross-lane shuffles) followed by a cross-wave step through LDS; the
-// variance is the second pass over the register-resident row (no E[x^2] - mean^2).
+// HBM-bound.  One workgroup per row; each thread owns NCH runs of 8 consecutive elements
+// (32 bytes of every fp32 partial, 16 bytes of a bf16 row), spaced THREADS runs apart so a
+// wave's loads are contiguous.  Loads go out in batches: for each partial in turn every
+// run's loads (NCH 32-byte loads per thread), issued while the previous partial is being
+// added; then the residual row; then gamma and beta ahead of the statistics.  The partials
+// are read once and the outputs written once, so those accesses are streaming
+// (non-temporal): on MI355X that moves the fused reduce from 4.9 to 5.45 TB/s.  A
+// streaming residual load measured slower and is not used.
+// The row stays in registers: the mean is a wave shuffle reduction plus one cross-wave step
+// through LDS, and the variance is a second pass over the registers (no E[x^2] - mean^2).
 #include "common.hpp"
 
 namespace tpk {
@@ -28,30 +34,70 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+struct F8 {
+  float v[8];
+};
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// 8 consecutive elements of a bf16 or fp32 output row, written as streaming stores.
 template <bool BF16>
-__device__ __forceinline__ float4 load4(const void* p, int64_t idx) {
+__device__ __forceinline__ void store8(void* p, int64_t idx, const F8& r) {
   if (BF16) {
-    const uint2 u = *(const uint2*)((const bf16_t*)p + idx);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    const u32x4_t u = {pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3]),
+                       pack_bf16x2(r.v[4], r.v[5]), pack_bf16x2(r.v[6], r.v[7])};
+    __builtin_nontemporal_store(u, (u32x4_t*)((bf16_t*)p + idx));
   } else {
-    return *(const float4*)((const float*)p + idx);
+    __builtin_nontemporal_store(f32x4_t{r.v[0], r.v[1], r.v[2], r.v[3]}, (f32x4_t*)((float*)p + idx));
+    __builtin_nontemporal_store(f32x4_t{r.v[4], r.v[5], r.v[6], r.v[7]}, (f32x4_t*)((float*)p + idx + 4));
   }
 }
 
+// Raw 16 bytes (8 bf16) or 32 bytes (8 fp32) of a row, loaded as one batch item.
 template <bool BF16>
-__device__ __forceinline__ void store4(void* p, int64_t idx, float4 v) {
-  if (BF16) {
-    uint2 u;
-    u.x = pack_bf16x2(v.x, v.y);
-    u.y = pack_bf16x2(v.z, v.w);
-    *(uint2*)((bf16_t*)p + idx) = u;
+struct Raw8;
+template <>
+struct Raw8<true> {
+  uint4 u;
+};
+template <>
+struct Raw8<false> {
+  f32x4_t a, b;
+};
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const void* p, int64_t idx) {
+  Raw8<BF16> r;
+  if constexpr (BF16) {
+    r.u = *(const uint4*)((const bf16_t*)p + idx);
   } else {
-    *(float4*)((float*)p + idx) = v;
+    r.a = *(const f32x4_t*)((const float*)p + idx);
+    r.b = *(const f32x4_t*)((const float*)p + idx + 4);
+  }
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* v) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = r.a[e];
+      v[4 + e] = r.b[e];
+    }
   }
 }
 
-template <int THREADS, int VPT, bool BF16>
+// FULL: every run of every thread lies inside the row (H == NCH * THREADS * 8), so no run
+// needs a bounds test and each batch of loads is issued without branches.
+template <int THREADS, int NCH, bool BF16, bool FULL>
 __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   __shared__ float red[THREADS / 64];
   const int64_t row = blockIdx.x;
@@ -59,68 +105,132 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   const int64_t H = r.H;
   const int64_t roff = row * H;
 
-  float4 v[VPT];
+  bool in[NCH];
+  int64_t col[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    col[c] = ((int64_t)c * THREADS + tid) * 8;
+    in[c] = FULL || col[c] < H;
+  }
+
+  // h = sum of the partials in ascending order, then + residual.  The loads of partial p+1
+  // go out before partial p is added, so a batch is always in flight.
+  float v[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+  auto load_part = [&](int p, f32x4_t (&q)[NCH][2]) {
+    const float* part = r.parts + (int64_t)p * r.part_stride + roff;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (in[c]) {
+        q[c][0] = __builtin_nontemporal_load((const f32x4_t*)(part + col[c]));
+        q[c][1] = __builtin_nontemporal_load((const f32x4_t*)(part + col[c] + 4));
+      } else {
+        q[c][0] = q[c][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  if (r.n_parts > 0) {
+    f32x4_t qa[NCH][2], qb[NCH][2];
+    load_part(0, qa);
+    for (int p = 0; p < r.n_parts; ++p) {
+      if (p + 1 < r.n_parts) load_part(p + 1, qb);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[c][e] += qa[c][0][e];
+          v[c][4 + e] += qa[c][1][e];
+        }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        qa[c][0] = qb[c][0];
+        qa[c][1] = qb[c][1];
+      }
+    }
+  }
+  Raw8<BF16> res[NCH];
+  if (r.residual) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (in[c]) res[c] = load_raw8<BF16>(r.residual, roff + col[c]);
+  }
   float sum = 0.0f;
 #pragma unroll
-  for (int c = 0; c < VPT; ++c) {
-    const int64_t col = ((int64_t)c * THREADS + tid) * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (col < H) {
-      if (r.n_parts > 0) {
-        acc = *(const float4*)(r.parts + roff + col);
-        for (int p = 1; p < r.n_parts; ++p) {
-          const float4 q = *(const float4*)(r.parts + (int64_t)p * r.part_stride + roff + col);
-          acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
-        }
-      }
+  for (int c = 0; c < NCH; ++c) {
+    if (in[c]) {
       if (r.residual) {
-        const float4 q = load4<BF16>(r.residual, roff + col);
-        acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+        float x[8];
+        unpack8<BF16>(res[c], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] += x[e];
       }
-      if (r.h_out) store4<BF16>(r.h_out, roff + col, acc);
+      if (r.h_out) {
+        F8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.v[e] = v[c][e];
+        store8<BF16>(r.h_out, roff + col[c], o);
+      }
     }
-    v[c] = acc;
-    sum += (acc.x + acc.y) + (acc.z + acc.w);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) sum += v[c][e] + v[c][e + 1];
   }
   if (!r.gamma) return;
 
+  // gamma / beta go out before the statistics' reductions hide their latency.
+  Raw8<BF16> gm[NCH], bt[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (in[c]) {
+      gm[c] = load_raw8<BF16>(r.gamma, col[c]);
+      if (r.beta) bt[c] = load_raw8<BF16>(r.beta, col[c]);
+    }
+  }
   const float inv_h = 1.0f / (float)H;
   const float mean = block_sum<THREADS>(sum, red) * inv_h;
   float sq = 0.0f;
 #pragma unroll
-  for (int c = 0; c < VPT; ++c) {
-    const int64_t col = ((int64_t)c * THREADS + tid) * 4;
-    if (col < H) {
-      const float a0 = v[c].x - mean, a1 = v[c].y - mean, a2 = v[c].z - mean, a3 = v[c].w - mean;
-      sq += (a0 * a0 + a1 * a1) + (a2 * a2 + a3 * a3);
+  for (int c = 0; c < NCH; ++c) {
+    if (in[c]) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float a0 = v[c][e] - mean, a1 = v[c][e + 1] - mean;
+        sq += a0 * a0 + a1 * a1;
+      }
     }
   }
   const float var = block_sum<THREADS>(sq, red) * inv_h;
   const float rstd = 1.0f / sqrtf(var + r.eps);
 #pragma unroll
-  for (int c = 0; c < VPT; ++c) {
-    const int64_t col = ((int64_t)c * THREADS + tid) * 4;
-    if (col < H) {
-      const float4 g = load4<BF16>(r.gamma, col);
-      float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r.beta) b = load4<BF16>(r.beta, col);
-      float4 y;
-      y.x = (v[c].x - mean) * rstd * g.x + b.x;
-      y.y = (v[c].y - mean) * rstd * g.y + b.y;
-      y.z = (v[c].z - mean) * rstd * g.z + b.z;
-      y.w = (v[c].w - mean) * rstd * g.w + b.w;
-      store4<BF16>(r.y_out, roff + col, y);
+  for (int c = 0; c < NCH; ++c) {
+    if (in[c]) {
+      float gv[8], bv[8];
+      unpack8<BF16>(gm[c], gv);
+      if (r.beta) unpack8<BF16>(bt[c], bv);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
+      F8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y.v[e] = (v[c][e] - mean) * rstd * gv[e] + bv[e];
+      store8<BF16>(r.y_out, roff + col[c], y);
     }
   }
 }
 
-template <int THREADS, int VPT>
+template <int THREADS, int NCH>
 hipError_t launch_t(const ReduceDesc& r, hipStream_t stream) {
   dim3 grid((unsigned)r.rows), block(THREADS);
-  if (r.bf16)
-    hipLaunchKernelGGL((reduce_ln_kernel<THREADS, VPT, true>), grid, block, 0, stream, r);
-  else
-    hipLaunchKernelGGL((reduce_ln_kernel<THREADS, VPT, false>), grid, block, 0, stream, r);
+  const bool full = r.H == (int64_t)NCH * THREADS * 8;
+  if (r.bf16) {
+    if (full) hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, true, true>), grid, block, 0, stream, r);
+    else hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, true, false>), grid, block, 0, stream, r);
+  } else {
+    if (full) hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, false, true>), grid, block, 0, stream, r);
+    else hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, false, false>), grid, block, 0, stream, r);
+  }
   return hipGetLastError();
 }
 
@@ -129,17 +239,18 @@ hipError_t launch_t(const ReduceDesc& r, hipStream_t stream) {
 hipError_t launch_reduce_ln(const ReduceDesc& r, hipStream_t stream) {
   if (r.rows <= 0) return hipSuccess;
   if (r.rows > 0x7fffffff) return hipErrorInvalidValue;
-  const int64_t h4 = (r.H + 3) / 4;
-  if (h4 <= 256 * 1) return launch_t<256, 1>(r, stream);
-  if (h4 <= 256 * 2) return launch_t<256, 2>(r, stream);
-  if (h4 <= 256 * 3) return launch_t<256, 3>(r, stream);
-  if (h4 <= 256 * 4) return launch_t<256, 4>(r, stream);
-  if (h4 <= 256 * 6) return launch_t<256, 6>(r, stream);
-  if (h4 <= 256 * 8) return launch_t<256, 8>(r, stream);
-  if (h4 <= 256 * 12) return launch_t<256, 12>(r, stream);
-  if (h4 <= 256 * 16) return launch_t<256, 16>(r, stream);
-  if (h4 <= 1024 * 8) return launch_t<1024, 8>(r, stream);
-  if (h4 <= 1024 * 16) return launch_t<1024, 16>(r, stream);
+  const int64_t runs = (r.H + 7) / 8;  // runs of 8 elements per row
+  if (runs <= 64 * 1) return launch_t<64, 1>(r, stream);
+  if (runs <= 128 * 1) return launch_t<128, 1>(r, stream);
+  if (runs <= 256 * 1) return launch_t<256, 1>(r, stream);
+  if (runs <= 256 * 2) return launch_t<256, 2>(r, stream);
+  if (runs <= 256 * 3) return launch_t<256, 3>(r, stream);
+  if (runs <= 256 * 4) return launch_t<256, 4>(r, stream);
+  if (runs <= 256 * 6) return launch_t<256, 6>(r, stream);
+  if (runs <= 256 * 8) return launch_t<256, 8>(r, stream);
+  if (runs <= 512 * 6) return launch_t<512, 6>(r, stream);
+  if (runs <= 512 * 8) return launch_t<512, 8>(r, stream);
+  if (runs <= 1024 * 8) return launch_t<1024, 8>(r, stream);
   return hipErrorInvalidValue;
 }
 
