@@ -27,6 +27,8 @@ enum Epilogue : int {
 //       (n / b_blk) * b_blk_stride + (n % b_blk)
 //     which lets the QKV projection read three separated column blocks of [Wq | Wk | Wv]
 //     as one operand (b_blk = N gives the plain contiguous case).
+//     n_off shifts that logical numbering: column n of this product is logical column
+//     n_off + n of B (0 unless the launcher splits N over several launches).
 //   C [M, N] row-major, leading dimension ldc (bf16 / fp32 per dtype and epilogue).
 struct GemmDesc {
   const void* A;
@@ -35,6 +37,7 @@ struct GemmDesc {
   int64_t ldb;
   int64_t b_blk;
   int64_t b_blk_stride;
+  int64_t n_off;
   void* C;
   int64_t ldc;
   int64_t M, N, K;
@@ -67,6 +70,16 @@ struct ReduceDesc {
   int64_t rows, H;
   int bf16;  // io dtype is bf16 (else fp32)
 };
+
+// Tile shapes of one bf16 product: columns [0, n0) with bm0 x bn0 tiles, then, if n1 > 0,
+// columns [n0, n0 + n1) with bm1 x bn1 tiles in a second launch.
+struct GemmPlan {
+  int bm0, bn0;
+  int64_t n0;
+  int bm1, bn1;
+  int64_t n1;
+};
+GemmPlan gemm_bf16_plan(int64_t M, int64_t N, int cus);
 
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t stream);

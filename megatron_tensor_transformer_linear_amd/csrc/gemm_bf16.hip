@@ -8,9 +8,10 @@
 // 1.1 and figure 1.2: the two block views of a matrix product that make the column and
 // outer-product-sum splits).
 //
-// Tile: 256 x BN x 32 per K step (BN = 256, 192 or 128), 256 threads = 4 waves in a 2 x 2
-// grid, each wave owning a 128 x BN/2 sub-tile as 4 x (BN/64) blocks of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulators in AGPRs).
+// Tile: BM x BN x 32 per K step (256 x 256, 256 x 192, 256 x 128 or 128 x 128, chosen per
+// shape by gemm_bf16_plan), 256 threads = 4 waves in a 2 x 2 grid, each wave owning a
+// BM/2 x BN/2 sub-tile as (BM/64) x (BN/64) blocks of v_mfma_f32_32x32x16_bf16 (fp32
+// accumulators in AGPRs).
 //
 // Staging: HBM -> LDS directly (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at
 // LDS base + 16 * lane, no VGPR round trip), in a ring of 4 stages, so the loads of stage
@@ -43,9 +44,8 @@
 namespace tpk {
 namespace {
 
-constexpr int BM = 256, BK = 32;
+constexpr int BK = 32;
 constexpr int NTHREADS = 256;
-constexpr int A_BYTES = BM * BK * 2;  // one A stage: 16 KB
 constexpr uint32_t OOB = 0x80000000u; // buffer offset past every resource range
 
 typedef __attribute__((address_space(3))) char lds_char_t;
@@ -147,10 +147,13 @@ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& tile_m
   tile_n = w / gsz;
 }
 
-template <int BN, int NST, int EPI>
+template <int BM, int BN, int NST, int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
+  constexpr int WM = BM / 2;                      // rows per wave
+  constexpr int MI = WM / 32;                     // 32-high MFMA blocks per wave
   constexpr int WN = BN / 2;                      // columns per wave
   constexpr int NJ = WN / 32;                     // 32-wide MFMA blocks per wave
+  constexpr int A_BYTES = BM * BK * 2;            // one A stage
   constexpr int BPITCH = BN == 128 ? 256 : 512;   // bytes per B k-row in LDS
   constexpr int CPR = BPITCH / 16;                // 16-byte chunks per B k-row
   constexpr int RPI = 1024 / BPITCH;              // B k-rows per wave load instruction
@@ -160,6 +163,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   constexpr int B_LD = B_BYTES / 1024 / 4;
   constexpr int LPS = A_LD + B_LD;
   static_assert(BN == 256 || BN == 192 || BN == 128, "tile width");
+  static_assert(BM == 256 || BM == 128, "tile height");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
 
   const int tid = threadIdx.x;
@@ -207,7 +211,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       const int j = (lane % CPR) ^ swz_b(krow);
       const int64_t nlog = n0 + 8 * j;
       const bool ok = live && 8 * j < BN && nlog < N;
-      const int64_t col = (nlog / g.b_blk) * g.b_blk_stride + (nlog % g.b_blk);
+      const int64_t nb = g.n_off + nlog;  // logical column of the whole B operand
+      const int64_t col = (nb / g.b_blk) * g.b_blk_stride + (nb % g.b_blk);
       d.b_off[i] = ok ? (uint32_t)((krow * ldb + col) * 2) : OOB;
     }
   };
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   int a_rd[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
-    a_rd[ks] = (wm * 128 + r32) * 64 + (((2 * ks + kh) ^ swz_a(r32)) * 16);
+    a_rd[ks] = (wm * WM + r32) * 64 + (((2 * ks + kh) ^ swz_a(r32)) * 16);
   const int grp = lane >> 4, li = lane & 15, q = li & 3, s = li >> 2;
   int b_rd[NJ];
 #pragma unroll
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     b_rd[j] = A_BYTES + (8 * (grp >> 1) + s) * BPITCH + ((chunk ^ swz_b(s)) * 16) + (q & 1) * 8;
   }
 
-  // Accumulators of the wave's 128 x WN sub-tile, as 4 x NJ blocks of 32 x 32.
+  // Accumulators of the wave's WM x WN sub-tile, as MI x NJ blocks of 32 x 32.
   //   bf16 outputs (TRANS): each MFMA takes the W fragment as its first operand and the X
   //     fragment as its second, so the block it accumulates is the transpose of the output
   //     block: lane l's 16 values of block (i, j) are output row 32 i + l % 32, columns
@@ -235,25 +240,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   //     32 i + 8 (r / 4) + 4 (l / 32) + r % 4, column 32 j + l % 32, so one 4-byte store per
   //     value writes two whole 128-byte rows per instruction.
   constexpr bool TRANS = EPI != EPI_PARTIAL_F32;
-  f32x16_t acc[4][NJ];
+  f32x16_t acc[MI][NJ];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   };
   zero_acc();
-  bf16x8_t fa[2][4], fb[2][NJ];
+  bf16x8_t fa[2][MI], fb[2][NJ];
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
   const uint32_t lds_a = lds0 + (uint32_t)(wv * A_LD * 1024);            // this wave's A loads
   const uint32_t lds_b = lds0 + (uint32_t)(A_BYTES + wv * B_LD * 1024);  // this wave's B loads
 
   // ---- the work items a K step is made of
-  constexpr int NM = 4 * NJ;  // MFMAs per half-step
-  constexpr int NR = 4 + NJ;  // fragment-read items per half-step (a B item is two reads)
+  constexpr int NM = MI * NJ;  // MFMAs per half-step
+  constexpr int NR = MI + NJ;  // fragment-read items per half-step (a B item is two reads)
   // MFMA m of a half-step: row block m / NJ, column block m % NJ.
   auto mfma = [&](int slot, int m) {
     const int i = m / NJ, j = m % NJ;
@@ -265,10 +270,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   // Read item t of sub-step ks of the stage held in buffer `buf` into fragment slot `slot`.
   auto read_item = [&](int buf, int ks, int slot, int t) {
     const char* sb = smem + buf * STAGE;
-    if (t < 4) {
+    if (t < MI) {
       fa[slot][t] = *(const bf16x8_t*)(sb + a_rd[ks] + t * 32 * 64);
     } else {
-      const int j = t - 4;
+      const int j = t - MI;
       fb[slot][j] = ds_read_tr_pair(sb + b_rd[j] + ks * 16 * BPITCH, 4 * BPITCH);
     }
   };
@@ -378,11 +383,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     // Epilogue of tile t (see the accumulator layout above).
     int tile_m, tile_n;
     tile_coords(t, tm, tn, tile_m, tile_n);
-    const int64_t m_w = (int64_t)tile_m * BM + wm * 128, n_w = (int64_t)tile_n * BN + wn * WN;
+    const int64_t m_w = (int64_t)tile_m * BM + wm * WM, n_w = (int64_t)tile_n * BN + wn * WN;
     if constexpr (TRANS) {
       const int64_t row0 = m_w + (lane & 31), col0 = n_w + 4 * (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int64_t row = row0 + 32 * i;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     } else {
       const int64_t row0 = m_w + 4 * (lane >> 5), col0 = n_w + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int64_t col = col0 + 32 * j;
@@ -441,46 +446,93 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int BN, int NST>
-hipError_t launch_bn(const GemmDesc& g, hipStream_t stream) {
+template <int BM, int BN, int NST>
+hipError_t launch_tile(const GemmDesc& g, hipStream_t stream) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
   const int64_t tiles = tm * tn;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  // One workgroup per compute unit (each holds 128-160 KB of LDS), looping over tiles.
+  // One workgroup per compute unit (each holds 64-128 KB of LDS), looping over tiles.
   const int64_t blocks = min(tiles, (int64_t)device_cus());
   dim3 grid((unsigned)blocks), block(NTHREADS);
   switch (g.epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_STORE>), grid, block, 0, stream, g); break;
-    case EPI_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_GELU_TANH>), grid, block, 0, stream, g); break;
-    case EPI_PARTIAL_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BN, NST, EPI_PARTIAL_F32>), grid, block, 0, stream, g); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NST, EPI_STORE>), grid, block, 0, stream, g); break;
+    case EPI_GELU_TANH: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NST, EPI_GELU_TANH>), grid, block, 0, stream, g); break;
+    case EPI_PARTIAL_F32: hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, NST, EPI_PARTIAL_F32>), grid, block, 0, stream, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_shape(int bm, int bn, const GemmDesc& g, hipStream_t stream) {
+  if (bm == 128) return launch_tile<128, 128, 4>(g, stream);
+  switch (bn) {
+    case 192: return launch_tile<256, 192, 4>(g, stream);
+    case 128: return launch_tile<256, 128, 4>(g, stream);
+    default: return launch_tile<256, 256, 4>(g, stream);
+  }
+}
+
 }  // namespace
 
-// Tile width per shape: the fewest rounds of workgroups over the 256 compute units, each
-// round costing its tile width, ties going to the wider tile.
-int gemm_bf16_tile_n(int64_t M, int64_t N) {
-  const int64_t tm = (M + BM - 1) / BM;
-  int best = 256;
-  int64_t best_cost = -1;
-  for (int bn : {256, 192, 128}) {
-    const int64_t tiles = tm * ((N + bn - 1) / bn);
-    const int64_t cost = ((tiles + 255) / 256) * bn;
-    if (best_cost < 0 || cost < best_cost) { best = bn; best_cost = cost; }
+// Launch plan for one product: the tile shapes and, optionally, a split of the N range into a
+// part of 256 x 256 tiles that fills whole rounds of workgroups and a strip of 128 x 128
+// tiles.  The plan minimises the sum over launches of rounds x the measured cost of one round
+// of that tile shape relative to a round of 256 x 256 tiles (MI355X, K = 12288, per-round
+// time ratios 256x192 0.862, 256x128 0.693, 128x128 0.455).  For the 8192 x 4608 QKV
+// projection that is 4096 columns of 256 x 256 tiles (two rounds) plus a 512-wide strip of
+// 128 x 128 tiles (one round): 726 us against 792 us for 256 x 192 tiles alone.
+GemmPlan gemm_bf16_plan(int64_t M, int64_t N, int cus) {
+  struct Shape {
+    int bm, bn;
+    double cost;
+  };
+  const Shape shapes[] = {{256, 256, 1.0}, {256, 192, 0.862}, {256, 128, 0.693}, {128, 128, 0.455}};
+  auto rounds = [&](const Shape& sh, int64_t n) {
+    const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((n + sh.bn - 1) / sh.bn);
+    return (tiles + cus - 1) / cus;
+  };
+  GemmPlan best{256, 256, N, 0, 0, 0};
+  double best_cost = -1.0;
+  for (const Shape& sh : shapes) {
+    const double c = rounds(sh, N) * sh.cost;
+    if (best_cost < 0 || c < best_cost - 1e-9) {
+      best = GemmPlan{sh.bm, sh.bn, N, 0, 0, 0};
+      best_cost = c;
+    }
+  }
+  // Split: the widest multiple of 256 columns whose 256 x 256 tiles fill whole rounds.
+  const int64_t tm = (M + 255) / 256;
+  for (int64_t nm = (N / 256) * 256; nm >= 256; nm -= 256) {
+    if ((tm * (nm / 256)) % cus != 0) continue;
+    if (nm == N) break;
+    const double c = rounds(shapes[0], nm) * shapes[0].cost + rounds(shapes[3], N - nm) * shapes[3].cost;
+    if (c < best_cost - 1e-9) {
+      best = GemmPlan{256, 256, nm, 128, 128, N - nm};
+      best_cost = c;
+    }
+    break;
   }
   return best;
 }
 
+namespace {
+hipError_t launch_plan(const GemmPlan& pl, const GemmDesc& g, hipStream_t stream) {
+  GemmDesc a = g;
+  a.N = pl.n0;
+  hipError_t e = launch_shape(pl.bm0, pl.bn0, a, stream);
+  if (e != hipSuccess || pl.n1 == 0) return e;
+  GemmDesc b = g;
+  b.N = pl.n1;
+  b.n_off = g.n_off + pl.n0;
+  const size_t es = g.epi == EPI_PARTIAL_F32 ? 4 : 2;
+  b.C = (char*)g.C + (size_t)pl.n0 * es;
+  return launch_shape(pl.bm1, pl.bn1, b, stream);
+}
+}  // namespace
+
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream) {
-  switch (gemm_bf16_tile_n(g.M, g.N)) {
-    case 192: return launch_bn<192, 4>(g, stream);
-    case 128: return launch_bn<128, 4>(g, stream);
-    default: return launch_bn<256, 4>(g, stream);
-  }
+  return launch_plan(gemm_bf16_plan(g.M, g.N, device_cus()), g, stream);
 }
 
 }  // namespace tpk

@@ -87,6 +87,7 @@ int tp_col_linear_gelu(const void* X, const void* W, void* Y, int64_t ldy, int64
   g.ldb = N;
   g.b_blk = nl;
   g.b_blk_stride = 0;
+  g.n_off = 0;
   g.C = Y;
   g.ldc = ldy;
   g.M = seq;
@@ -119,6 +120,7 @@ int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpar
   g.ldb = N;
   g.b_blk = N;
   g.b_blk_stride = 0;
+  g.n_off = 0;
   g.C = Zpart;
   g.ldc = N;
   g.M = seq;
@@ -166,6 +168,7 @@ int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* 
   q.ldb = 3 * H;
   q.b_blk = s.nb;
   q.b_blk_stride = H;
+  q.n_off = 0;
   q.C = ws_qkv;
   q.ldc = 3 * s.nb;
   q.M = s.T;
@@ -193,6 +196,7 @@ int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* 
   o.ldb = H;
   o.b_blk = H;
   o.b_blk_stride = 0;
+  o.n_off = 0;
   o.C = Zpart;
   o.ldc = H;
   o.M = s.T;

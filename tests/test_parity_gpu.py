@@ -314,6 +314,27 @@ def test_row_edge_shapes(lib, dtype, T, K, N, world, rank):
     check("row partial", Z, O.row_linear_partial(Xv[:, :K], Wv, rank, world), dtype)
 
 
+def test_column_split_launch(lib):
+    """A product whose columns the launcher splits over two launches: 4096 columns of
+    256 x 256 tiles (one full round on 256 compute units) and a 512-wide strip of 128 x 128
+    tiles.  (The full-size attention and block tests take the same split through the QKV
+    column-block map.)"""
+    tp, pl = lib
+    T, H, nh, d, world, rank = 4096, 256, 24, 128, 2, 1  # H_model = nh*d = 3072; rank block 1536
+    Hm = nh * d
+    rng = np.random.Generator(np.random.PCG64(4608))
+    X = rng.standard_normal((T, Hm)).astype(np.float32)
+    Wqkv = (rng.standard_normal((Hm, 3 * Hm)) / np.sqrt(Hm)).astype(np.float32)
+    Xd, Wd = dev_values(X, "bf16"), dev_values(Wqkv, "bf16")
+    Xv, Wv = host(Xd), host(Wd)
+    nl = 3 * Hm // world  # 4608 output columns
+    Y = torch.empty(T, nl, dtype=torch.bfloat16, device=Xd.device)
+    say(f"  column split launch T={T} H={Hm} N/P={nl}")
+    tp.tp_col_linear_gelu(Xd, Wd, Y, nl, T, Hm, 3 * Hm, rank, world, tp.TP_ACT_GELU_TANH, tp.TP_BF16)
+    _sync()
+    check("column (split launch)", Y, O.col_linear(Xv, Wv, rank, world, "gelu_tanh"), "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("T,K,N,world,rank", [(70, 1024, 264, 4, 3), (300, 6144, 136, 8, 2)])
 def test_row_dense_shard(lib, dtype, T, K, N, world, rank):
