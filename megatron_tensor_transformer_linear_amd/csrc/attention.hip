@@ -147,15 +147,17 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnDesc a) {
           s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ss], s[jb], 0, 0, 0);
         }
       }
-      // scores -> log2 domain, mask, block max.  Element r of block jb is key
-      // j0 + 32 jb + 8 (r / 4) + 4 h + r % 4 for query mq.
+      // Mask, block max of the raw scores.  Element r of block jb is key
+      // j0 + 32 jb + 8 (r / 4) + 4 h + r % 4 for query mq.  Every active block holds a key
+      // <= the wave's first query (blocks are 64-aligned, waves 32-aligned), so no lane's
+      // block is fully masked and its max is finite.
       const bool need_mask = (a.causal && j0 + AK - 1 > qw) || (j0 + AK > seq);
       float mx = -INFINITY;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = s[jb][r] * scale;
+          float v = s[jb][r];
           if (need_mask) {
             const int key = j0 + 32 * jb + 8 * (r >> 2) + 4 * h + (r & 3);
             if (key >= seq || (a.causal && key > mq)) v = -INFINITY;
@@ -163,24 +165,32 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnDesc a) {
           s[jb][r] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is visible to every query
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale;  // log2 domain (scale > 0)
+      // Lazy running max: the offset m_run moves only when this block's max exceeds it by
+      // more than LAZY (log2 units), so the probabilities stay below 2^LAZY, and the output
+      // rescale is skipped unless some lane of the wave moved.  The final normalisation
+      // divides by a sum taken with the same offsets, so the result is unchanged.
+      constexpr float LAZY = 8.0f;
+      const bool move = mx > m_run + LAZY;
+      const float m_new = move ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 where the offset stays
       m_run = m_new;
       float psum = 0.0f;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[jb][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][r], scale, -m_new));
           s[jb][r] = p;
           psum += p;
         }
       l_run = l_run * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
 
       // P^T fragments: MFMA u covers keys 16 u + 4 h + {0..3, 8..11}, which are the
       // accumulator rows r/4 = 2 (u % 2) and 2 (u % 2) + 1 of block u / 2.

@@ -91,15 +91,19 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest, ties to even: the gfx950 conversion instruction
+// v_cvt_pk_bf16_f32 (checked on MI355X to give the same bits as the integer
+// round-to-nearest-even formula on 16.7M finite values, including exact ties, both
+// neighbours of a tie, denormals and values that round to infinity).
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
 // GeLU, tanh form.  0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), so
