@@ -137,14 +137,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnDesc a) {
       const bf16_t* ks = Ks + cur * AK * K_PITCH;
       const bf16_t* vs = Vs + cur * AK * V_PITCH;
       f32x16_t s[2];
+      const f32x16_t zero16 = {};
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[jb][r] = 0.0f;
-#pragma unroll
         for (int ss = 0; ss < 8; ++ss) {
           const bf16x8_t kf = *(const bf16x8_t*)(ks + (32 * jb + (lane & 31)) * K_PITCH + 16 * ss + 8 * h);
-          s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ss], s[jb], 0, 0, 0);
+          s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ss], ss == 0 ? zero16 : s[jb], 0, 0, 0);
         }
       }
       // Mask, block max of the raw scores.  Element r of block jb is key
@@ -152,19 +151,20 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(AttnDesc a) {
       // <= the wave's first query (blocks are 64-aligned, waves 32-aligned), so no lane's
       // block is fully masked and its max is finite.
       const bool need_mask = (a.causal && j0 + AK - 1 > qw) || (j0 + AK > seq);
+      if (need_mask) {  // wave-uniform: only diagonal and ragged-end blocks
+        // key = j0 + kofs(jb, r) is visible iff key <= klim (branch-free selects)
+        const int klim = (a.causal ? min(mq, (int)seq - 1) : (int)seq - 1) - j0 - 4 * h;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[jb][r] = (32 * jb + 8 * (r >> 2) + (r & 3)) <= klim ? s[jb][r] : -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[jb][r];
-          if (need_mask) {
-            const int key = j0 + 32 * jb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key >= seq || (a.causal && key > mq)) v = -INFINITY;
-          }
-          s[jb][r] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale;  // log2 domain (scale > 0)
       // Lazy running max: the offset m_run moves only when this block's max exceeds it by
       // more than LAZY (log2 units), so the probabilities stay below 2^LAZY, and the output
