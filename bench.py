@@ -16,7 +16,9 @@ step's algorithmic flops (all 8 ranks' shards) divided by the measured step time
 TFLOP/s.  Per-kernel durations come from HIP events recorded on the launch stream inside
 the timed region; the roofline object reports the dominant GEMM (the column-parallel
 GEMM + GeLU of the MLP).  The CPU baseline times the float64 oracle on a bounded row
-sample of the same workload on this host.
+sample of the same workload on this host.  After the timed steps, the sequence-parallel
+form of the epilogue (each rank's reduce-scatter of its 1024 rows) is timed on its own and
+reported beside the step, outside `value`.
 """
 from __future__ import annotations
 
@@ -245,6 +247,29 @@ def main() -> int:
             "avg_launch_ms": round(col_ms, 4),
         },
         "stages": stages,
+    }
+    # Sequence-parallel epilogue (outside the timed step): rank r's reduce-scatter of the 8
+    # partials over its 1024 rows, fused with the residual add and LayerNorm, into its rows of
+    # the full buffers (the all-gather).  Same kernel as reduce1, on a row range.
+    sp_ev = []
+    for it in range(3):
+        for r in range(cfg.world):
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record(stream)
+            blk.reduce1_scatter(r)
+            e_.record(stream)
+            if it > 0:
+                sp_ev.append((s_, e_))
+    torch.cuda.synchronize()
+    sp_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in sp_ev]))
+    sp_bytes = reduce_bytes(T // cfg.world, H, cfg.world, "bf16", residual=True, h_out=True,
+                            y_out=True)
+    result["sequence_parallel_epilogue"] = {
+        "what": "one rank's reduce-scatter (8 fp32 partials, 1024 rows) + residual + LayerNorm",
+        "avg_ms_per_rank": round(sp_ms, 4),
+        "gbs": round(sp_bytes / sp_ms / 1e6, 1),
+        "hbm_frac": round(sp_bytes / sp_ms / 1e6 / PEAK_HBM_GBS, 3),
+        "all_ranks_ms": round(sp_ms * cfg.world, 4),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")

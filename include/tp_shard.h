@@ -147,6 +147,29 @@ int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_
                                   float eps, void* h_out, void* y_out,
                                   int64_t rows, int64_t H, int dtype, void* stream);
 
+/* Sequence-parallel form of the same epilogue: the reduce-scatter of rank `rank`, fused with
+ * the residual add and LayerNorm of that rank's rows (pwwt.cn section 5.1, figure 7: an
+ * all-reduce is a reduce-scatter followed by an all-gather, and a consumer that needs only
+ * its share of the rows can take the reduce-scatter result directly; section 5.3: Megatron's
+ * sequence parallelism splits along the sequence, so each rank holds [S/P, H] instead of
+ * [S, H]).  With rl = rows/world and row0 = rank*rl:
+ *
+ *   h[i] = residual[row0 + i] + sum_{p ascending} parts[p][row0 + i]     i < rl, fp32
+ *   y[i] = LayerNorm(h[i]) * gamma + beta
+ *
+ * parts, n_parts, part_stride and residual describe the FULL [rows, H] operands, exactly as
+ * for tp_partial_reduce_residual_ln; h_out and y_out receive the rank's rl rows (dense,
+ * [rl, H]).  Pointing them at row row0 of full [rows, H] buffers for every rank is the
+ * all-gather (concatenation along rows).  Each output row is computed by the same arithmetic
+ * as the corresponding row of tp_partial_reduce_residual_ln, so the results are identical.
+ * Errors: as tp_partial_reduce_residual_ln, plus TP_ERR_RANK and TP_ERR_DIVISIBLE
+ * (rows % world). */
+int tp_partial_reduce_scatter_residual_ln(const float* parts, int n_parts, int64_t part_stride,
+                                          const void* residual, const void* gamma,
+                                          const void* beta, float eps, void* h_out, void* y_out,
+                                          int64_t rows, int64_t H, int rank, int world, int dtype,
+                                          void* stream);
+
 /* Static, NUL-terminated description of a tp_status value. */
 const char* tp_status_string(int status);
 

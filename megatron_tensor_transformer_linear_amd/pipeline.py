@@ -179,11 +179,15 @@ class AttnShard:
 
 class BlockShard:
     """The whole Transformer block with every rank's attention and MLP shard:
-        xn = LN1(X); h = X + sum_r Attn_r(xn); hn = LN2(h); out = h + sum_r MLP_r(hn)."""
+        xn = LN1(X); h = X + sum_r Attn_r(xn); hn = LN2(h); out = h + sum_r MLP_r(hn).
+
+    sequence_parallel=True runs each epilogue as the ranks' reduce-scatters (rank r sums,
+    adds the residual to and normalises rows [r T/P, (r+1) T/P)) writing into the full
+    buffers at their row offsets, which is the all-gather (pwwt.cn sections 5.1, 5.3)."""
 
     def __init__(self, X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, world: int,
                  batch: int, seq: int, n_heads: int, head_dim: int, causal: bool = True,
-                 eps: float = 1e-5, stream=None):
+                 eps: float = 1e-5, stream=None, sequence_parallel: bool = False):
         self.X, self.Wqkv, self.Wo, self.W1, self.W2 = X, Wqkv, Wo, W1, W2
         self.g1, self.b1, self.g2, self.b2 = gamma1, beta1, gamma2, beta2
         self.T, self.H = X.shape
@@ -191,6 +195,9 @@ class BlockShard:
         self.P, self.batch, self.seq = world, batch, seq
         self.nh, self.d, self.causal, self.eps = n_heads, head_dim, causal, eps
         self.stream = stream
+        self.sequence_parallel = sequence_parallel
+        if sequence_parallel and self.T % world:
+            raise ValueError("sequence parallelism needs tokens divisible by the world size")
         dev = X.device
         bf = torch.bfloat16
         self.xn = torch.empty(self.T, self.H, dtype=bf, device=dev)
@@ -216,10 +223,27 @@ class BlockShard:
                               self.H, self.nh, self.d, r, self.P, int(self.causal), tp.TP_BF16,
                               self.ws, self.ws_bytes, self.stream)
 
+    def _scatter_rows(self, r: int):
+        """Rows of rank r's sequence block: (start, count)."""
+        n = self.T // self.P
+        return r * n, n
+
     def reduce1(self):
+        if self.sequence_parallel:
+            for r in range(self.P):
+                self.reduce1_scatter(r)
+            return
         tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.X, self.g2,
                                          self.b2, self.eps, self.h, self.hn, self.T, self.H,
                                          tp.TP_BF16, self.stream)
+
+    def reduce1_scatter(self, r: int):
+        """Rank r's reduce-scatter + residual + LN2 into its rows of h and hn."""
+        a, n = self._scatter_rows(r)
+        tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.P, self.T * self.H, self.X,
+                                                 self.g2, self.b2, self.eps, self.h[a:a + n],
+                                                 self.hn[a:a + n], self.T, self.H, r, self.P,
+                                                 tp.TP_BF16, self.stream)
 
     def mlp_col(self, r: int):
         fl = self.F // self.P
@@ -232,9 +256,21 @@ class BlockShard:
                                  r, self.P, tp.TP_BF16, self.stream)
 
     def reduce2(self):
+        if self.sequence_parallel:
+            for r in range(self.P):
+                self.reduce2_scatter(r)
+            return
         tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.h, None, None,
                                          0.0, self.out, None, self.T, self.H, tp.TP_BF16,
                                          self.stream)
+
+    def reduce2_scatter(self, r: int):
+        """Rank r's reduce-scatter + residual into its rows of out."""
+        a, n = self._scatter_rows(r)
+        tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.P, self.T * self.H, self.h,
+                                                 None, None, 0.0, self.out[a:a + n], None,
+                                                 self.T, self.H, r, self.P, tp.TP_BF16,
+                                                 self.stream)
 
     def attention_phase(self):
         self.pre_ln()

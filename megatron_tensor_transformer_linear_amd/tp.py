@@ -29,7 +29,8 @@ TP_ACT_NONE = 0
 TP_ACT_GELU_TANH = 1
 
 EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_workspace_bytes",
-            "tp_attn_head_shard", "tp_partial_reduce_residual_ln", "tp_status_string")
+            "tp_attn_head_shard", "tp_partial_reduce_residual_ln",
+            "tp_partial_reduce_scatter_residual_ln", "tp_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -50,6 +51,9 @@ lib.tp_attn_head_shard.restype = _int
 lib.tp_partial_reduce_residual_ln.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp, _vp,
                                               _i64, _i64, _int, _vp]
 lib.tp_partial_reduce_residual_ln.restype = _int
+lib.tp_partial_reduce_scatter_residual_ln.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp,
+                                                      _vp, _i64, _i64, _int, _int, _int, _vp]
+lib.tp_partial_reduce_scatter_residual_ln.restype = _int
 lib.tp_status_string.argtypes = [_int]
 lib.tp_status_string.restype = ctypes.c_char_p
 
@@ -121,3 +125,12 @@ def tp_partial_reduce_residual_ln(parts, n_parts: int, part_stride: int, residua
                                                     eps, _ptr(h_out), _ptr(y_out), rows, H, dtype,
                                                     _stream(stream)),
                   "tp_partial_reduce_residual_ln")
+
+
+def tp_partial_reduce_scatter_residual_ln(parts, n_parts: int, part_stride: int, residual, gamma,
+                                          beta, eps: float, h_out, y_out, rows: int, H: int,
+                                          rank: int, world: int, dtype: int, stream=None) -> int:
+    return _check(lib.tp_partial_reduce_scatter_residual_ln(
+        _ptr(parts), n_parts, part_stride, _ptr(residual), _ptr(gamma), _ptr(beta), eps,
+        _ptr(h_out), _ptr(y_out), rows, H, rank, world, dtype, _stream(stream)),
+        "tp_partial_reduce_scatter_residual_ln")

@@ -190,6 +190,45 @@ def reduce_residual_layernorm(parts: Sequence[np.ndarray], residual=None, gamma=
     return h, y
 
 
+def reduce_scatter_rows(parts: Sequence[np.ndarray], rank: int, world: int) -> np.ndarray:
+    """The reduce-scatter half of the all-reduce, split along the rows (the sequence): rank
+    r receives the sum over ranks (ascending) of row block r of every partial.
+
+    [pwwt] section 5.1, figure 7: an all-reduce is a reduce-scatter, after which each rank
+    holds one block of the summed tensor, followed by an all-gather of those blocks; a
+    consumer that needs only its block can take the reduce-scatter result directly.
+    Section 5.3: Megatron's sequence parallelism makes that block a block of the sequence,
+    [S/P, H] per rank.
+    """
+    if len(parts) == 0:
+        raise ValueError("no partials")
+    lo, hi = shard_range(_f64(parts[0]).shape[0], world, rank)
+    return reduce_partials([_f64(p)[lo:hi] for p in parts])
+
+
+def reduce_scatter_residual_layernorm(parts: Sequence[np.ndarray], residual, gamma, beta,
+                                      eps: float, rank: int, world: int):
+    """Sequence-parallel epilogue of rank r: its row block of the summed partials, plus the
+    same rows of the residual, then LayerNorm of those rows (the residual add and
+    LayerNorm act on each rank's share of the sequence; [pwwt] sections 5.1 and 5.3).
+    Returns (h_r, y_r); y_r is None when gamma is None."""
+    h = reduce_scatter_rows(parts, rank, world) if len(parts) else None
+    if residual is not None:
+        res = _f64(residual)
+        lo, hi = shard_range(res.shape[0], world, rank)
+        h = res[lo:hi] if h is None else h + res[lo:hi]
+    if h is None:
+        raise ValueError("nothing to reduce")
+    y = layer_norm(h, gamma, beta, eps) if gamma is not None else None
+    return h, y
+
+
+def concat_rows(blocks: Sequence[np.ndarray]) -> np.ndarray:
+    """The all-gather along the sequence: the ranks' row blocks stacked in rank order
+    ([pwwt] section 5.1, figure 7; rank 0 first as in [typc] section 2.1)."""
+    return np.concatenate([_f64(b) for b in blocks], axis=0)
+
+
 # ----------------------------------------------------------------------------- attention
 def split_qkv(Wqkv, hidden: int):
     """The fused QKV weight [H, 3H] read as [Wq | Wk | Wv]."""

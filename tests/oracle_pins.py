@@ -242,6 +242,54 @@ def pin_reduce_residual_layernorm():
     _close(y0, TF.layer_norm(_t(R), (8,), _t(g), _t(b), eps=1e-5).numpy(), 1e-13, "plain LN")
 
 
+def pin_reduce_scatter_integer_exact():
+    """Rank r's reduce-scatter block is the ascending-rank sum of row block r of every
+    partial (scalar loops), and the blocks stacked in rank order are the full sum."""
+    rng = _rng(23)
+    P, rows, H = 4, 12, 8
+    parts = [_ints(rng, (rows, H), -9, 9) for _ in range(P)]
+    blocks = []
+    for r in range(P):
+        got = O.reduce_scatter_rows(parts, r, P)
+        ref = np.zeros((rows // P, H))
+        for i in range(rows // P):
+            for j in range(H):
+                acc = 0.0
+                for p in range(P):
+                    acc += parts[p][r * (rows // P) + i][j]
+                ref[i, j] = acc
+        assert np.array_equal(got, ref), r
+        blocks.append(got)
+    assert np.array_equal(O.concat_rows(blocks), O.reduce_partials(parts))
+    for bad in [(10, 4), (12, 5)]:
+        try:
+            O.reduce_scatter_rows([np.zeros((bad[0], H))] * 2, 0, bad[1])
+        except ValueError:
+            continue
+        raise AssertionError(f"rows={bad[0]} world={bad[1]} not rejected")
+
+
+def pin_reduce_scatter_layernorm_equals_full():
+    """The sequence-parallel epilogue gathered over ranks equals the fused all-reduce
+    epilogue: the residual add and LayerNorm act row by row."""
+    rng = _rng(24)
+    P, rows, H = 4, 16, 24
+    parts = [rng.standard_normal((rows, H)) for _ in range(P)]
+    R = rng.standard_normal((rows, H))
+    g, b = rng.standard_normal(H), rng.standard_normal(H)
+    h_full, y_full = O.reduce_residual_layernorm(parts, R, g, b, 1e-5)
+    hs, ys = zip(*[O.reduce_scatter_residual_layernorm(parts, R, g, b, 1e-5, r, P)
+                   for r in range(P)])
+    _close(O.concat_rows(hs), h_full, 1e-15, "gathered h")
+    _close(O.concat_rows(ys), y_full, 1e-14, "gathered y")
+    lo, hi = O.shard_range(rows, P, 2)
+    ref = TF.layer_norm(_t(h_full[lo:hi]), (H,), _t(g), _t(b), eps=1e-5).numpy()
+    _close(ys[2], ref, 1e-13, "rank 2 LN")
+    lo1, hi1 = O.shard_range(rows, P, 1)
+    h0, _ = O.reduce_scatter_residual_layernorm([], R, g, b, 1e-5, 1, P)
+    assert np.array_equal(h0, R[lo1:hi1])
+
+
 # ----------------------------------------------------------------------------- attention
 def _attn_inputs(seed, batch, seq, H, scale=0.7):
     rng = _rng(seed)

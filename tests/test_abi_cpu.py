@@ -94,6 +94,15 @@ def red(tp, **kw):
                                                 a["H"], a["dtype"], a["stream"])
 
 
+def rs(tp, **kw):
+    a = dict(parts=P, n=4, stride=64 * 256, res=P, g=P, b=P, eps=1e-5, h=P, y=P, rows=64, H=256,
+             rank=1, world=4, dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_partial_reduce_scatter_residual_ln(
+        a["parts"], a["n"], a["stride"], a["res"], a["g"], a["b"], a["eps"], a["h"], a["y"],
+        a["rows"], a["H"], a["rank"], a["world"], a["dtype"], a["stream"])
+
+
 CASES = [
     # column-parallel linear
     ("col null X", col, dict(X=None), "TP_ERR_NULL"),
@@ -158,6 +167,16 @@ CASES = [
     ("reduce stride % 4", red, dict(stride=64 * 256 + 2), "TP_ERR_ALIGN"),
     ("reduce misaligned residual", red, dict(res=P + 8), "TP_ERR_ALIGN"),
     ("reduce misaligned y", red, dict(y=P + 2), "TP_ERR_ALIGN"),
+    # sequence-parallel reduce-scatter + residual + LN
+    ("scatter rows % world", rs, dict(rows=66, stride=66 * 256), "TP_ERR_DIVISIBLE"),
+    ("scatter rank = world", rs, dict(rank=4), "TP_ERR_RANK"),
+    ("scatter world 0", rs, dict(world=0), "TP_ERR_RANK"),
+    ("scatter bad dtype", rs, dict(dtype=3), "TP_ERR_DTYPE"),
+    ("scatter null parts", rs, dict(parts=None), "TP_ERR_NULL"),
+    ("scatter gamma without y", rs, dict(y=None), "TP_ERR_NULL"),
+    ("scatter stride too small", rs, dict(stride=64 * 256 - 8), "TP_ERR_SHAPE"),
+    ("scatter H % 8", rs, dict(H=260, stride=64 * 260), "TP_ERR_ALIGN"),
+    ("scatter misaligned h", rs, dict(h=P + 4), "TP_ERR_ALIGN"),
 ]
 
 

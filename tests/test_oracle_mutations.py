@@ -129,6 +129,21 @@ def _residual_added_twice(parts, residual=None, gamma=None, beta=None, eps=1e-5)
     return h, y
 
 
+def _scatter_rank0_block(parts, rank, world):
+    return _orig["reduce_scatter_rows"](parts, 0, world)
+
+
+def _scatter_residual_unsliced(parts, residual, gamma, beta, eps, rank, world):
+    h = _orig["reduce_scatter_rows"](parts, rank, world) if len(parts) else None
+    res = np.asarray(residual, np.float64)[: (h.shape[0] if h is not None else residual.shape[0] // world)]
+    h = res if h is None else h + res
+    return h, (_orig["layer_norm"](h, gamma, beta, eps) if gamma is not None else None)
+
+
+def _gather_rows_reversed(blocks):
+    return _orig["concat_rows"](list(blocks)[::-1])
+
+
 MUTATIONS = {
     "shard_off_by_one": ("shard_range", _shard_off_by_one),
     "shard_reversed_ranks": ("shard_range", _shard_reversed),
@@ -150,6 +165,9 @@ MUTATIONS = {
     "mlp_wrong_b_block": ("mlp_shard", _mlp_block0_of_b),
     "o_projection_transposed": ("attn_head_shard", _attn_wo_columns),
     "residual_added_twice": ("reduce_residual_layernorm", _residual_added_twice),
+    "scatter_takes_rank0_rows": ("reduce_scatter_rows", _scatter_rank0_block),
+    "scatter_residual_not_sliced": ("reduce_scatter_residual_layernorm", _scatter_residual_unsliced),
+    "gather_rows_reversed": ("concat_rows", _gather_rows_reversed),
 }
 
 

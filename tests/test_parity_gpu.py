@@ -212,11 +212,12 @@ def test_small_attention(lib, causal):
     check("sum of partials", sh.Z, O.reduce_partials(parts), "bf16")
 
 
-def _block_runner(pl, cfg, t):
+def _block_runner(pl, cfg, t, sequence_parallel=False):
     return pl.BlockShard(dev(t["X"]), dev_values(_qkv_values(t), "bf16"), dev(t["Wo"]),
                          dev(t["W1"]), dev(t["W2"]), dev(t["gamma"]), dev(t["beta"]),
                          dev(t["gamma"]), dev(t["beta"]), cfg.world, cfg.batch, cfg.seq,
-                         cfg.n_heads, cfg.head_dim, cfg.causal, cfg.eps)
+                         cfg.n_heads, cfg.head_dim, cfg.causal, cfg.eps,
+                         sequence_parallel=sequence_parallel)
 
 
 def _block_ref(cfg, t, rows=None):
@@ -264,6 +265,72 @@ def test_block_deterministic(lib):
     sh.step()
     _sync()
     assert torch.equal(first.view(torch.int16), sh.out.view(torch.int16))
+
+
+def test_block_sequence_parallel(lib):
+    """The block with sequence-parallel epilogues (each rank reduce-scatters its rows; the
+    row blocks land at their offsets, which is the all-gather) gives the same bits as the
+    fused all-reduce epilogues, and matches the oracle's gathered reduce-scatter blocks."""
+    tp, pl = lib
+    cfg = small_variant("block_bf16_tp8")
+    t = generate(cfg)
+    full = _block_runner(pl, cfg, t)
+    sp = _block_runner(pl, cfg, t, sequence_parallel=True)
+    say(f"  block sequence-parallel vs all-reduce epilogues {cfg}")
+    full.step()
+    sp.step()
+    _sync()
+    for name in ("h", "hn", "out"):
+        a, b = getattr(full, name), getattr(sp, name)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    ref = _block_ref(cfg, t)
+    check("out (sequence parallel)", sp.out, ref["out"], "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,H,n_parts,world", [
+    (64, 256, 4, 4),       # one row block per rank
+    (96, 4104, 3, 8),      # 12 rows per rank, ragged vector tail
+    (8192, 12288, 8, 8),   # the block's epilogue shape, 1024 rows per rank
+])
+def test_reduce_scatter_rows(lib, dtype, rows, H, n_parts, world):
+    """Each rank's reduce-scatter + residual + LN gives exactly the rows the fused all-reduce
+    epilogue gives for them, and the oracle's reduce-scatter blocks within tolerance."""
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(rows + H + world))
+    Pd = (torch.randn(n_parts, rows, H, device="cuda:0") * 2).float()
+    Rd = dev_values((rng.standard_normal((rows, H)) + 0.5).astype(np.float32), dtype)
+    gd = dev_values((1 + 0.5 * rng.standard_normal(H)).astype(np.float32), dtype)
+    bd = dev_values((0.5 * rng.standard_normal(H)).astype(np.float32), dtype)
+    dt = tp.TP_BF16 if dtype == "bf16" else tp.TP_F32
+    h_all = torch.empty(rows, H, dtype=Rd.dtype, device="cuda:0")
+    y_all = torch.empty_like(h_all)
+    tp.tp_partial_reduce_residual_ln(Pd, n_parts, rows * H, Rd, gd, bd, 1e-5, h_all, y_all, rows,
+                                     H, dt)
+    h_sp = torch.full_like(h_all, 7.0)
+    y_sp = torch.full_like(h_all, 7.0)
+    n = rows // world
+    for r in range(world):
+        say(f"  reduce-scatter dtype={dtype} rows={rows} H={H} parts={n_parts} rank={r}/{world}")
+        tp.tp_partial_reduce_scatter_residual_ln(Pd, n_parts, rows * H, Rd, gd, bd, 1e-5,
+                                                 h_sp[r * n:], y_sp[r * n:], rows, H, r, world, dt)
+    _sync()
+    assert torch.equal(h_all, h_sp) and torch.equal(y_all, y_sp)
+    sample = [0, 1, world // 2, world - 1]
+    parts_h = host(Pd) if rows * H <= 1 << 22 else None
+    for r in sorted(set(sample)):
+        rows_r = slice(r * n, (r + 1) * n)
+        if parts_h is None:  # large case: the oracle on the first and last rows of the block
+            idx = np.array([r * n, (r + 1) * n - 1])
+            P = [host(Pd[p][idx]) for p in range(n_parts)]
+            h, y = O.reduce_residual_layernorm(P, host(Rd[idx]), host(gd), host(bd), 1e-5)
+            check(f"h rank {r} (rows)", h_sp[idx], h, dtype)
+            check(f"y rank {r} (rows)", y_sp[idx], y, dtype)
+            continue
+        h, y = O.reduce_scatter_residual_layernorm(list(parts_h), host(Rd), host(gd), host(bd),
+                                                   1e-5, r, world)
+        check(f"h rank {r}", h_sp[rows_r], h, dtype)
+        check(f"y rank {r}", y_sp[rows_r], y, dtype)
 
 
 # ============================================================== edge cases
