@@ -98,6 +98,68 @@ int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpar
                           int64_t seq, int64_t K, int64_t N, int rank, int world,
                           int dtype, void* stream);
 
+/* Column-parallel linear + GeLU that also keeps the pre-activation for the backward pass:
+ * exactly tp_col_linear_gelu with act = TP_ACT_GELU_TANH, plus
+ *
+ *   U[t, j] = sum_k X[t, k] * W[k, rank*N/world + j]     rounded to bf16, ld ldu >= N/world
+ *
+ * (U is what the GeLU's derivative is evaluated at in tp_row_linear_backward; Y is computed
+ * from the fp32 sum, not from the rounded U).  Only dtype TP_BF16.
+ * Errors: as tp_col_linear_gelu, TP_ERR_NULL for U, TP_ERR_SHAPE for ldu < N/world. */
+int tp_col_linear_gelu_save(const void* X, const void* W, void* Y, int64_t ldy, void* U,
+                            int64_t ldu, int64_t seq, int64_t H, int64_t N, int rank, int world,
+                            int dtype, void* stream);
+
+/* Backward of the row-parallel linear of rank `rank`, with the derivative of the activation
+ * that precedes it (the column layer's GeLU) fused in.  The pages state that the backward
+ * pass has its own communication pattern and that the gradients are sharded like the
+ * weights (typc.net section 2.2; pwwt.cn sections 1.3 and 6.1), without formulas; these are
+ * the chain rule applied to Zpart = Y_r . W_r, Z = sum_r Zpart_r:
+ *
+ *   dY[t, j]  = act'(U[t, j]) * sum_n dZ[t, n] * W[rank*K/world + j, n]     (dZ . W_r^T)
+ *   dW[j, n] (+)= sum_t Y[t, j] * dZ[t, n]                                 (Y_r^T . dZ)
+ *
+ * for t < seq, j < K/world, n < N.  The forward all-reduce turns into an identity: every rank
+ * uses the full dZ [seq, N] (dense, ld N), so this call needs no exchange.  W [K, N] dense is
+ * the full weight (row block `rank` is used).  Y [seq, K/world] (ld ldy) is the rank's
+ * forward input shard; U [seq, K/world] (ld ldu) the pre-activation of the column layer that
+ * produced Y (tp_col_linear_gelu_save), used only with act = TP_ACT_GELU_TANH (act'(u) is
+ * the tanh-form GeLU's derivative; with TP_ACT_NONE act' = 1 and U may be NULL).  Outputs:
+ * dY bf16 [seq, K/world] (ld ld_dy >= K/world), the gradient at the rank's column-layer
+ * output; dW fp32 [K/world, N] (ld ld_dw >= N), the gradient of the rank's row block of W,
+ * overwritten, or added to when accumulate != 0 (gradient accumulation over micro-batches).
+ * Either output may be NULL to skip its product (not both).  Only dtype TP_BF16.
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE (sizes <= 0, seq > 2^30, a leading dimension too small,
+ * N or ldy > 2^21), TP_ERR_DIVISIBLE (K % world), TP_ERR_RANK, TP_ERR_DTYPE, TP_ERR_ALIGN,
+ * TP_ERR_LAUNCH. */
+int tp_row_linear_backward(const void* dZ, const void* W, const void* Y, int64_t ldy,
+                           const void* U, int64_t ldu, void* dY, int64_t ld_dy, float* dW,
+                           int64_t ld_dw, int64_t seq, int64_t K, int64_t N, int rank, int world,
+                           int act, int accumulate, int dtype, void* stream);
+
+/* Backward of the column-parallel linear of rank `rank` (chain rule on Y_r = X . W_r, the
+ * rank's column block):
+ *
+ *   dXpart[t, h] = sum_j dU[t, j] * W[h, rank*N/world + j]                 (dU_r . W_r^T)
+ *   dW[h, j]   (+)= sum_t X[t, h] * dU[t, j]                              (X^T . dU_r)
+ *
+ * for t < seq, h < H, j < N/world.  X [seq, H] dense is the full forward input, W [H, N]
+ * dense the full weight (column block `rank` is used), dU [seq, N/world] (ld ldu) the
+ * gradient at the rank's pre-activation output (dY of tp_row_linear_backward).  dXpart fp32
+ * [seq, H] dense is this rank's partial of the input gradient: the forward identity turns
+ * into an all-reduce, dX = sum over ranks of dXpart, which tp_partial_reduce_residual_ln
+ * computes from the stacked partials (gamma = NULL, residual = the gradient arriving along
+ * the residual path or NULL).  dW fp32 [H, N/world] (ld ld_dw >= N/world) is the gradient
+ * of the rank's column block, overwritten or (accumulate != 0) added to.  Either output may
+ * be NULL (not both).  Only dtype TP_BF16.
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE (sizes <= 0, seq > 2^30, a leading dimension too small,
+ * H, N or ldu > 2^21), TP_ERR_DIVISIBLE (N % world), TP_ERR_RANK, TP_ERR_DTYPE, TP_ERR_ALIGN,
+ * TP_ERR_LAUNCH. */
+int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t ldu,
+                           float* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
+                           int64_t N, int rank, int world, int accumulate, int dtype,
+                           void* stream);
+
 /* Workspace bytes tp_attn_head_shard needs for these sizes; 0 if the sizes are invalid. */
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_heads,
                                int head_dim, int world, int dtype);

@@ -15,9 +15,21 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 // Epilogues of the GEMM tile.
 enum Epilogue : int {
-  EPI_STORE = 0,       // Y (io dtype) = acc
-  EPI_GELU_TANH = 1,   // Y (io dtype) = gelu_tanh(acc)
-  EPI_PARTIAL_F32 = 2  // Z (fp32) = acc
+  EPI_STORE = 0,        // Y (io dtype) = acc
+  EPI_GELU_TANH = 1,    // Y (io dtype) = gelu_tanh(acc)
+  EPI_PARTIAL_F32 = 2,  // Z (fp32) = acc
+  EPI_GELU_SAVE = 3,    // Y (bf16) = gelu_tanh(acc), and aux (bf16) = acc, the pre-activation
+  EPI_GELU_BWD = 4,     // Y (bf16) = acc * gelu_tanh'(aux), aux the bf16 pre-activation
+  EPI_ACC_F32 = 5       // Z (fp32) += acc
+};
+
+// Memory layouts of the two GEMM operands (bf16 tile only).  Bit 0: A is stored
+// M-contiguous (the product reads X^T of a row-major X).  Bit 1: B is stored K-contiguous
+// (the product reads W^T of a row-major W).
+enum Layout : int {
+  LAY_NN = 0,  // A [M, K] and B [K, N] row-major
+  LAY_TN = 1,  // A^T [K, M] row-major (element (m, k) at A + k lda + m), B [K, N] row-major
+  LAY_NT = 2   // A [M, K] row-major, B^T [N, K] row-major (element (k, n) at B + n ldb + k)
 };
 
 // C = epi(A . B) for one rank's shard.
@@ -30,6 +42,11 @@ enum Epilogue : int {
 //     n_off shifts that logical numbering: column n of this product is logical column
 //     n_off + n of B (0 unless the launcher splits N over several launches).
 //   C [M, N] row-major, leading dimension ldc (bf16 / fp32 per dtype and epilogue).
+//   layout: a Layout.  With LAY_NT the logical-to-physical column map of B must be the
+//     identity (b_blk >= n_off + N); row n_off + n of B^T is column n.  With LAY_TN, A is
+//     A^T [K, M] with leading dimension lda.
+//   aux [M, N] bf16, leading dimension ldaux: the pre-activation written by EPI_GELU_SAVE
+//     or read by EPI_GELU_BWD (unused otherwise).
 struct GemmDesc {
   const void* A;
   int64_t lda;
@@ -42,6 +59,9 @@ struct GemmDesc {
   int64_t ldc;
   int64_t M, N, K;
   int epi;
+  int layout = LAY_NN;
+  void* aux = nullptr;
+  int64_t ldaux = 0;
 };
 
 // Causal / full attention over one rank's heads.

@@ -16,6 +16,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // the weight with 32-bit byte offsets, which bounds the two leading dimensions.
 constexpr int64_t MAX_LD_ACT = 1 << 21;
 constexpr int64_t MAX_LD_WEIGHT = 1 << 23;
+// The weight-gradient products contract over the sequence, which the tile counts in 32-bit.
+constexpr int64_t MAX_SEQ_BWD = (int64_t)1 << 30;
 inline bool mult8(int64_t v) { return (v & 7) == 0; }
 
 inline int check_rank(int rank, int world) {
@@ -130,6 +132,170 @@ int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpar
   (void)hipGetLastError();
   hipStream_t s = (hipStream_t)stream;
   return launched(dtype == TP_BF16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s));
+}
+
+int tp_col_linear_gelu_save(const void* X, const void* W, void* Y, int64_t ldy, void* U,
+                            int64_t ldu, int64_t seq, int64_t H, int64_t N, int rank, int world,
+                            int dtype, void* stream) {
+  if (!X || !W || !Y || !U) return TP_ERR_NULL;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  if (seq <= 0 || H <= 0 || N <= 0) return TP_ERR_SHAPE;
+  if (N % world) return TP_ERR_DIVISIBLE;
+  const int64_t nl = N / world;
+  if (ldy < nl || ldu < nl) return TP_ERR_SHAPE;
+  if (H > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y) || !aligned16(U)) return TP_ERR_ALIGN;
+  if (!mult8(H) || !mult8(N) || !mult8(nl) || !mult8(ldy) || !mult8(ldu)) return TP_ERR_ALIGN;
+
+  GemmDesc g;
+  g.A = X;
+  g.lda = H;
+  g.B = (const bf16_t*)W + (size_t)rank * nl;  // column block `rank` of W[H, N]
+  g.ldb = N;
+  g.b_blk = nl;
+  g.b_blk_stride = 0;
+  g.n_off = 0;
+  g.C = Y;
+  g.ldc = ldy;
+  g.M = seq;
+  g.N = nl;
+  g.K = H;
+  g.epi = EPI_GELU_SAVE;
+  g.aux = U;
+  g.ldaux = ldu;
+  (void)hipGetLastError();
+  return launched(launch_gemm_bf16(g, (hipStream_t)stream));
+}
+
+int tp_row_linear_backward(const void* dZ, const void* W, const void* Y, int64_t ldy,
+                           const void* U, int64_t ldu, void* dY, int64_t ld_dy, float* dW,
+                           int64_t ld_dw, int64_t seq, int64_t K, int64_t N, int rank, int world,
+                           int act, int accumulate, int dtype, void* stream) {
+  if (!dZ || !W || (!dY && !dW)) return TP_ERR_NULL;
+  if (dW && !Y) return TP_ERR_NULL;
+  if (dY && act == TP_ACT_GELU_TANH && !U) return TP_ERR_NULL;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  if (seq <= 0 || K <= 0 || N <= 0 || seq > MAX_SEQ_BWD) return TP_ERR_SHAPE;
+  if (K % world) return TP_ERR_DIVISIBLE;
+  const int64_t kl = K / world;
+  const bool use_u = dY && act == TP_ACT_GELU_TANH;
+  if ((dY && ld_dy < kl) || (use_u && ldu < kl) || (dW && (ldy < kl || ld_dw < N)))
+    return TP_ERR_SHAPE;
+  // dZ is the K-contiguous operand of dY = dZ . W_r^T and W_r^T the K-contiguous B^T; Y^T is
+  // the M-contiguous operand of dW = Y^T . dZ.
+  if (N > MAX_LD_ACT || (dW && ldy > MAX_LD_ACT)) return TP_ERR_SHAPE;
+  const void* ptrs[] = {dZ, W, Y, U, dY, dW};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return TP_ERR_ALIGN;
+  if (!mult8(N) || !mult8(kl)) return TP_ERR_ALIGN;
+  if ((dY && !mult8(ld_dy)) || (use_u && !mult8(ldu)) || (dW && (!mult8(ldy) || !mult8(ld_dw))))
+    return TP_ERR_ALIGN;
+
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (dY) {  // dY[t, j] = act'(U[t, j]) * sum_n dZ[t, n] W[rank*kl + j, n]
+    GemmDesc g;
+    g.A = dZ;
+    g.lda = N;
+    g.B = (const bf16_t*)W + (size_t)rank * kl * N;  // row block `rank` of W, read as B^T
+    g.ldb = N;
+    g.b_blk = kl;
+    g.b_blk_stride = 0;
+    g.n_off = 0;
+    g.C = dY;
+    g.ldc = ld_dy;
+    g.M = seq;
+    g.N = kl;
+    g.K = N;
+    g.layout = LAY_NT;
+    g.epi = use_u ? EPI_GELU_BWD : EPI_STORE;
+    g.aux = use_u ? const_cast<void*>(U) : nullptr;
+    g.ldaux = use_u ? ldu : 0;
+    if (launch_gemm_bf16(g, st) != hipSuccess) return TP_ERR_LAUNCH;
+  }
+  if (dW) {  // dW[j, n] (+)= sum_t Y[t, j] dZ[t, n]
+    GemmDesc g;
+    g.A = Y;
+    g.lda = ldy;
+    g.B = dZ;
+    g.ldb = N;
+    g.b_blk = N;
+    g.b_blk_stride = 0;
+    g.n_off = 0;
+    g.C = dW;
+    g.ldc = ld_dw;
+    g.M = kl;
+    g.N = N;
+    g.K = seq;
+    g.layout = LAY_TN;
+    g.epi = accumulate ? EPI_ACC_F32 : EPI_PARTIAL_F32;
+    if (launch_gemm_bf16(g, st) != hipSuccess) return TP_ERR_LAUNCH;
+  }
+  return TP_OK;
+}
+
+int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t ldu,
+                           float* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
+                           int64_t N, int rank, int world, int accumulate, int dtype,
+                           void* stream) {
+  if (!X || !W || !dU || (!dXpart && !dW)) return TP_ERR_NULL;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  if (seq <= 0 || H <= 0 || N <= 0 || seq > MAX_SEQ_BWD) return TP_ERR_SHAPE;
+  if (N % world) return TP_ERR_DIVISIBLE;
+  const int64_t nl = N / world;
+  if (ldu < nl || (dW && ld_dw < nl)) return TP_ERR_SHAPE;
+  // dU is the K-contiguous operand of dX = dU . W_r^T and W_r^T (rows of W) the K-contiguous
+  // B^T; X^T is the M-contiguous operand of dW = X^T . dU.
+  if (ldu > MAX_LD_ACT || N > MAX_LD_ACT || H > MAX_LD_ACT) return TP_ERR_SHAPE;
+  const void* ptrs[] = {X, W, dU, dXpart, dW};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return TP_ERR_ALIGN;
+  if (!mult8(H) || !mult8(N) || !mult8(nl) || !mult8(ldu) || (dW && !mult8(ld_dw)))
+    return TP_ERR_ALIGN;
+
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (dXpart) {  // dXpart[t, h] = sum_j dU[t, j] W[h, rank*nl + j]
+    GemmDesc g;
+    g.A = dU;
+    g.lda = ldu;
+    g.B = (const bf16_t*)W + (size_t)rank * nl;  // column block `rank` of W, read as B^T
+    g.ldb = N;
+    g.b_blk = H;
+    g.b_blk_stride = 0;
+    g.n_off = 0;
+    g.C = dXpart;
+    g.ldc = H;
+    g.M = seq;
+    g.N = H;
+    g.K = nl;
+    g.layout = LAY_NT;
+    g.epi = EPI_PARTIAL_F32;
+    if (launch_gemm_bf16(g, st) != hipSuccess) return TP_ERR_LAUNCH;
+  }
+  if (dW) {  // dW[h, j] (+)= sum_t X[t, h] dU[t, j]
+    GemmDesc g;
+    g.A = X;
+    g.lda = H;
+    g.B = dU;
+    g.ldb = ldu;
+    g.b_blk = nl;
+    g.b_blk_stride = 0;
+    g.n_off = 0;
+    g.C = dW;
+    g.ldc = ld_dw;
+    g.M = H;
+    g.N = nl;
+    g.K = seq;
+    g.layout = LAY_TN;
+    g.epi = accumulate ? EPI_ACC_F32 : EPI_PARTIAL_F32;
+    if (launch_gemm_bf16(g, st) != hipSuccess) return TP_ERR_LAUNCH;
+  }
+  return TP_OK;
 }
 
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_heads,

@@ -95,6 +95,77 @@ class MLPShard:
         self.reduce()
 
 
+class MLPTrainShard:
+    """Forward (keeping the pre-activation) and backward of the tensor-parallel MLP
+    Z = sum_r gelu(X . A_r) . B_r in bf16, the P ranks in turn on one GPU.
+
+    Forward of rank r: tp_col_linear_gelu_save writes U_r and Y_r = gelu(U_r) (dense
+    [T, F/P] each, as on the rank's own GPU), tp_row_linear_partial its fp32 partial of Z.
+    Backward, from the output gradient dZ [T, H] that every rank holds (the forward
+    all-reduce is an identity backwards): tp_row_linear_backward gives dU_r (the GeLU's
+    derivative fused in) and the rank's row block of dB; tp_col_linear_backward the rank's
+    fp32 partial of dX and its column block of dA; reduce_dx sums the partials (the backward
+    all-reduce) into dX (bf16).  dA [H, F] and dB [F, H] are fp32, each rank writing its own
+    block (the gradient is as sharded as the weight); accumulate=True adds to them."""
+
+    def __init__(self, X, A, B, dZ, world: int, accumulate: bool = False, stream=None):
+        self.X, self.A, self.B, self.dZ = X, A, B, dZ
+        self.T, self.H = X.shape
+        self.F = A.shape[1]
+        self.P = world
+        self.fl = self.F // world
+        self.accumulate = accumulate
+        self.stream = stream
+        dev = X.device
+        bf = torch.bfloat16
+        self.U = torch.empty(world, self.T, self.fl, dtype=bf, device=dev)
+        self.Y = torch.empty_like(self.U)
+        self.dU = torch.empty_like(self.U)
+        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        self.dXparts = torch.empty_like(self.parts)
+        self.dA = torch.zeros(self.H, self.F, dtype=torch.float32, device=dev)
+        self.dB = torch.zeros(self.F, self.H, dtype=torch.float32, device=dev)
+        self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
+        self.dX = torch.empty(self.T, self.H, dtype=bf, device=dev)
+
+    def forward_rank(self, r: int):
+        tp.tp_col_linear_gelu_save(self.X, self.A, self.Y[r], self.fl, self.U[r], self.fl, self.T,
+                                   self.H, self.F, r, self.P, tp.TP_BF16, self.stream)
+        tp.tp_row_linear_partial(self.Y[r], self.fl, self.B, self.parts[r], self.T, self.F,
+                                 self.H, r, self.P, tp.TP_BF16, self.stream)
+
+    def reduce_z(self):
+        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, None, None, None,
+                                         0.0, self.Z, None, self.T, self.H, tp.TP_F32, self.stream)
+
+    def backward_row(self, r: int):
+        tp.tp_row_linear_backward(self.dZ, self.B, self.Y[r], self.fl, self.U[r], self.fl,
+                                  self.dU[r], self.fl, self.dB[r * self.fl:], self.H, self.T,
+                                  self.F, self.H, r, self.P, tp.TP_ACT_GELU_TANH,
+                                  int(self.accumulate), tp.TP_BF16, self.stream)
+
+    def backward_col(self, r: int):
+        tp.tp_col_linear_backward(self.X, self.A, self.dU[r], self.fl, self.dXparts[r],
+                                  self.dA[:, r * self.fl:], self.F, self.T, self.H, self.F, r,
+                                  self.P, int(self.accumulate), tp.TP_BF16, self.stream)
+
+    def reduce_dx(self):
+        tp.tp_partial_reduce_residual_ln(self.dXparts, self.P, self.T * self.H, None, None, None,
+                                         0.0, self.dX, None, self.T, self.H, tp.TP_BF16,
+                                         self.stream)
+
+    def forward(self):
+        for r in range(self.P):
+            self.forward_rank(r)
+        self.reduce_z()
+
+    def backward(self):
+        for r in range(self.P):
+            self.backward_row(r)
+            self.backward_col(r)
+        self.reduce_dx()
+
+
 class LinearShard:
     """One linear X[T,H].W[H,N]: the column block of chosen ranks, and the row split of
     every rank with the fp32 partial sum Z."""

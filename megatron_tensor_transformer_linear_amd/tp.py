@@ -28,7 +28,8 @@ TP_BF16 = 1
 TP_ACT_NONE = 0
 TP_ACT_GELU_TANH = 1
 
-EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_workspace_bytes",
+EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_col_linear_gelu_save",
+            "tp_row_linear_backward", "tp_col_linear_backward", "tp_attn_workspace_bytes",
             "tp_attn_head_shard", "tp_partial_reduce_residual_ln",
             "tp_partial_reduce_scatter_residual_ln", "tp_status_string")
 
@@ -43,6 +44,15 @@ lib.tp_col_linear_gelu.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, 
 lib.tp_col_linear_gelu.restype = _int
 lib.tp_row_linear_partial.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]
 lib.tp_row_linear_partial.restype = _int
+lib.tp_col_linear_gelu_save.argtypes = [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int,
+                                        _int, _int, _vp]
+lib.tp_col_linear_gelu_save.restype = _int
+lib.tp_row_linear_backward.argtypes = [_vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64,
+                                       _i64, _i64, _int, _int, _int, _int, _int, _vp]
+lib.tp_row_linear_backward.restype = _int
+lib.tp_col_linear_backward.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                                       _int, _int, _int, _int, _vp]
+lib.tp_col_linear_backward.restype = _int
 lib.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int]
 lib.tp_attn_workspace_bytes.restype = _sz
 lib.tp_attn_head_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
@@ -101,6 +111,31 @@ def tp_row_linear_partial(X, ldx: int, W, Zpart, seq: int, K: int, N: int, rank:
                           dtype: int, stream=None) -> int:
     return _check(lib.tp_row_linear_partial(_ptr(X), ldx, _ptr(W), _ptr(Zpart), seq, K, N, rank,
                                             world, dtype, _stream(stream)), "tp_row_linear_partial")
+
+
+def tp_col_linear_gelu_save(X, W, Y, ldy: int, U, ldu: int, seq: int, H: int, N: int, rank: int,
+                            world: int, dtype: int, stream=None) -> int:
+    return _check(lib.tp_col_linear_gelu_save(_ptr(X), _ptr(W), _ptr(Y), ldy, _ptr(U), ldu, seq, H,
+                                              N, rank, world, dtype, _stream(stream)),
+                  "tp_col_linear_gelu_save")
+
+
+def tp_row_linear_backward(dZ, W, Y, ldy: int, U, ldu: int, dY, ld_dy: int, dW, ld_dw: int,
+                           seq: int, K: int, N: int, rank: int, world: int, act: int,
+                           accumulate: int, dtype: int, stream=None) -> int:
+    return _check(lib.tp_row_linear_backward(_ptr(dZ), _ptr(W), _ptr(Y), ldy, _ptr(U), ldu,
+                                             _ptr(dY), ld_dy, _ptr(dW), ld_dw, seq, K, N, rank,
+                                             world, act, int(accumulate), dtype, _stream(stream)),
+                  "tp_row_linear_backward")
+
+
+def tp_col_linear_backward(X, W, dU, ldu: int, dXpart, dW, ld_dw: int, seq: int, H: int, N: int,
+                           rank: int, world: int, accumulate: int, dtype: int,
+                           stream=None) -> int:
+    return _check(lib.tp_col_linear_backward(_ptr(X), _ptr(W), _ptr(dU), ldu, _ptr(dXpart),
+                                             _ptr(dW), ld_dw, seq, H, N, rank, world,
+                                             int(accumulate), dtype, _stream(stream)),
+                  "tp_col_linear_backward")
 
 
 def tp_attn_workspace_bytes(batch: int, seq: int, H: int, n_heads: int, head_dim: int, world: int,

@@ -43,7 +43,9 @@ __all__ = [
     "shard_range", "matmul", "gelu_tanh", "col_linear", "concat_columns",
     "row_linear_partial", "reduce_partials", "layer_norm", "reduce_residual_layernorm",
     "split_qkv", "head_range", "attention_heads", "attn_head_shard", "mlp_shard",
-    "block_shard", "block_forward",
+    "block_shard", "block_forward", "reduce_scatter_rows", "reduce_scatter_residual_layernorm",
+    "concat_rows", "gelu_tanh_grad", "row_linear_backward", "col_linear_backward",
+    "mlp_shard_backward", "mlp_backward",
 ]
 
 F64 = np.float64
@@ -93,6 +95,29 @@ def _act(y: np.ndarray, act: str) -> np.ndarray:
         return y
     if act == "gelu_tanh":
         return gelu_tanh(y)
+    raise ValueError(act)
+
+
+def gelu_tanh_grad(x) -> np.ndarray:
+    """Derivative of gelu_tanh, by the chain rule.  With c = sqrt(2/pi), a = 0.044715 and
+    u = c (x + a x^3):
+
+      d/dx [0.5 x (1 + tanh u)] = 0.5 (1 + tanh u) + 0.5 x (1 - tanh(u)^2) c (1 + 3 a x^2).
+
+    Needed by the backward pass of the MLP pair, which the pages mention without formulas
+    ([typc] section 2.2; [pwwt] sections 1.3 and 6.1).
+    """
+    x = _f64(x)
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (x + 0.044715 * x * x * x))
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x)
+
+
+def _act_grad(u: np.ndarray, act: str) -> np.ndarray:
+    if act == "none":
+        return np.ones_like(_f64(u))
+    if act == "gelu_tanh":
+        return gelu_tanh_grad(u)
     raise ValueError(act)
 
 
@@ -147,6 +172,79 @@ def reduce_partials(parts: Sequence[np.ndarray]) -> np.ndarray:
     for p in parts[1:]:
         acc += _f64(p)
     return acc
+
+
+# ----------------------------------------------------------------------------- backward
+# The pages say that the backward pass of the split linears has its own communication
+# pattern and that each rank computes only the gradient of its own block of W, a gradient as
+# sharded as the weight ([typc] section 2.2; [pwwt] section 1.3; the troubleshooting table of
+# [pwwt] section 6.1 names the transposed-weight dimensions and the rank order of the
+# gradient split), but give no formulas.  The functions below are the chain rule applied to
+# the forward definitions above, for a loss L whose gradient at the layer output is dZ:
+#   Z = Y . W      =>  dL/dY = dZ . W^T,  dL/dW = Y^T . dZ.
+def row_linear_backward(dZ, Y, W, rank: int, world: int, U=None,
+                        act: str = "none") -> Tuple[np.ndarray, np.ndarray]:
+    """Backward of the row-parallel linear of rank r (Zpart_r = Y_r . W[block r, :],
+    Z = sum_r Zpart_r).  Every rank receives the full dZ [seq, N] (the forward all-reduce
+    is an identity in the backward pass).  Returns (dY_r, dW_r):
+
+      dY_r = (dZ . W[block r, :]^T) * act'(U_r)     [seq, K/world]
+      dW_r = Y_r^T . dZ                             [K/world, N]
+
+    Y_r [seq, K/world] is the rank's forward input; when Y_r = act(U_r) came from the
+    column layer, the factor act'(U_r) turns dY_r into the gradient at the pre-activation
+    U_r (act "none": factor 1, U unused).
+    """
+    k0, k1 = shard_range(W.shape[0], world, rank)
+    W = _f64(W)
+    dZ = _f64(dZ)
+    Y = _f64(Y)
+    if Y.shape != (dZ.shape[0], k1 - k0) or dZ.shape[1] != W.shape[1]:
+        raise ValueError("shapes differ")
+    dY = matmul(dZ, W[k0:k1, :].T)
+    if act != "none":
+        dY = dY * _act_grad(U, act)
+    return dY, matmul(Y.T, dZ)
+
+
+def col_linear_backward(dU, X, W, rank: int, world: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Backward of the column-parallel linear of rank r (U_r = X . W[:, block r]).  Returns
+    (dX_part_r, dW_r):
+
+      dX_part_r = dU_r . W[:, block r]^T      [seq, H]
+      dW_r      = X^T . dU_r                   [H, N/world]
+
+    The full dX is the sum of dX_part_r over the ranks: the forward identity (every rank
+    reads the whole X) becomes an all-reduce in the backward pass.
+    """
+    n0, n1 = shard_range(W.shape[1], world, rank)
+    X = _f64(X)
+    dU = _f64(dU)
+    if dU.shape != (X.shape[0], n1 - n0) or X.shape[1] != W.shape[0]:
+        raise ValueError("shapes differ")
+    return matmul(dU, _f64(W)[:, n0:n1].T), matmul(X.T, dU)
+
+
+def mlp_shard_backward(X, A, B, dZ, rank: int, world: int, act: str = "gelu_tanh") -> Dict:
+    """Rank r's backward of mlp_shard: forward U_r = X . A[:, block r], Y_r = act(U_r), then
+    the row layer's backward (fused with act') and the column layer's backward.  Returns
+    {"U", "Y", "dU", "dB", "dA", "dX_part"}: dB is the gradient of B[block r, :], dA of
+    A[:, block r], dX_part the rank's partial of the input gradient."""
+    U = col_linear(X, A, rank, world, "none")
+    Y = _act(U, act)
+    dU, dB = row_linear_backward(dZ, Y, B, rank, world, U, act)
+    dX_part, dA = col_linear_backward(dU, X, A, rank, world)
+    return {"U": U, "Y": Y, "dU": dU, "dB": dB, "dA": dA, "dX_part": dX_part}
+
+
+def mlp_backward(X, A, B, dZ, world: int, act: str = "gelu_tanh") -> Dict:
+    """Backward of the whole tensor-parallel MLP: every rank's mlp_shard_backward, then
+    dX = sum of the partials (ascending ranks), dA = the column blocks concatenated, dB = the
+    row blocks stacked, in rank order.  Returns {"dX", "dA", "dB"}."""
+    shards = [mlp_shard_backward(X, A, B, dZ, r, world, act) for r in range(world)]
+    return {"dX": reduce_partials([s["dX_part"] for s in shards]),
+            "dA": concat_columns([s["dA"] for s in shards]),
+            "dB": concat_rows([s["dB"] for s in shards])}
 
 
 # ----------------------------------------------------------------------------- LayerNorm

@@ -478,6 +478,140 @@ def pin_block_rows_subset():
         _close(sub["attn_parts"][r], full["attn_parts"][r][rows], 1e-14, "attn part")
 
 
+# ----------------------------------------------------------------------------- backward
+def _transpose(M):
+    """Explicit transpose by index swapping (no library call)."""
+    M = np.asarray(M, np.float64)
+    return np.array([[M[i][j] for i in range(M.shape[0])] for j in range(M.shape[1])])
+
+
+def pin_gelu_grad_closed_forms():
+    """gelu'(0) = 1/2; gelu(x) - gelu(-x) = x gives gelu'(x) + gelu'(-x) = 1 exactly; the
+    derivative tends to 1 for large x and to 0 for large negative x."""
+    assert O.gelu_tanh_grad(np.array([0.0]))[0] == 0.5
+    x = np.linspace(-6, 6, 241)
+    _close(O.gelu_tanh_grad(x) + O.gelu_tanh_grad(-x), np.ones_like(x), 1e-15, "gelu' symmetry")
+    assert abs(O.gelu_tanh_grad(np.array([30.0]))[0] - 1.0) < 1e-15
+    assert abs(O.gelu_tanh_grad(np.array([-30.0]))[0]) < 1e-15
+
+
+def pin_gelu_grad_finite_difference():
+    """Central differences of the (separately pinned) gelu_tanh, error O(h^2)."""
+    x = np.linspace(-7, 7, 281) + 0.013
+    h = 1e-5
+    fd = (O.gelu_tanh(x + h) - O.gelu_tanh(x - h)) / (2 * h)
+    _close(O.gelu_tanh_grad(x), fd, 1e-9, "gelu' vs central difference")
+
+
+def pin_gelu_grad_autograd():
+    x = torch.linspace(-8, 8, 1601, dtype=torch.float64, requires_grad=True)
+    TF.gelu(x, approximate="tanh").sum().backward()
+    _close(O.gelu_tanh_grad(x.detach().numpy()), x.grad.numpy(), 1e-14, "gelu' autograd")
+
+
+def pin_row_backward_integer_exact():
+    """Integer inputs: dY_r = dZ . W_r^T and dW_r = Y_r^T . dZ equal scalar-loop products over
+    explicitly transposed blocks, exactly, for every rank."""
+    rng = _rng(31)
+    seq, K, N = 5, 8, 6
+    dZ = _ints(rng, (seq, N), -4, 4)
+    W = _ints(rng, (K, N), -3, 3)
+    for world in (1, 2, 4):
+        kl = K // world
+        for r in range(world):
+            Y = _ints(rng, (seq, kl), -5, 5)
+            dY, dW = O.row_linear_backward(dZ, Y, W, r, world)
+            Wr = [[W[r * kl + j][n] for n in range(N)] for j in range(kl)]
+            assert np.array_equal(dY, brute_matmul(dZ, _transpose(Wr))), f"dY rank {r}/{world}"
+            assert np.array_equal(dW, brute_matmul(_transpose(Y), dZ)), f"dW rank {r}/{world}"
+
+
+def pin_row_backward_activation_factor():
+    """With act = gelu_tanh, dY is the plain product times gelu'(U) elementwise (dyadic
+    inputs keep the product exact)."""
+    rng = _rng(32)
+    seq, K, N, world = 4, 8, 5, 2
+    dZ = _ints(rng, (seq, N), -4, 4) / 4
+    W = _ints(rng, (K, N), -4, 4) / 8
+    U = rng.standard_normal((seq, K // world))
+    Y = _ints(rng, (seq, K // world), -3, 3)
+    for r in range(world):
+        plain, _ = O.row_linear_backward(dZ, Y, W, r, world)
+        dY, _ = O.row_linear_backward(dZ, Y, W, r, world, U, "gelu_tanh")
+        g = np.array([[O.gelu_tanh_grad(np.array([v]))[0] for v in row] for row in U])
+        _close(dY, plain * g, 1e-15, "act' factor")
+
+
+def pin_col_backward_integer_exact():
+    """Integer inputs: rank r's dX_part = dU_r . W[:, block r]^T and dW_r = X^T . dU_r by
+    scalar loops; the partials summed over ranks equal dU . W^T of the unsplit layer."""
+    rng = _rng(33)
+    seq, H, N = 5, 6, 8
+    X = _ints(rng, (seq, H), -4, 4)
+    W = _ints(rng, (H, N), -3, 3)
+    dU_full = _ints(rng, (seq, N), -3, 3)
+    for world in (1, 2, 4):
+        nl = N // world
+        parts = []
+        for r in range(world):
+            dU = dU_full[:, r * nl:(r + 1) * nl]
+            dXp, dW = O.col_linear_backward(dU, X, W, r, world)
+            Wr = [[W[h][r * nl + j] for j in range(nl)] for h in range(H)]
+            assert np.array_equal(dXp, brute_matmul(dU, _transpose(Wr))), f"dX_part {r}/{world}"
+            assert np.array_equal(dW, brute_matmul(_transpose(X), dU)), f"dW {r}/{world}"
+            parts.append(dXp)
+        assert np.array_equal(O.reduce_partials(parts), brute_matmul(dU_full, _transpose(W)))
+
+
+def _mlp_bwd_inputs(seed, seq, H, F):
+    rng = _rng(seed)
+    X = rng.standard_normal((seq, H))
+    A = rng.standard_normal((H, F)) / math.sqrt(H)
+    B = rng.standard_normal((F, H)) / math.sqrt(F)
+    dZ = rng.standard_normal((seq, H))
+    return X, A, B, dZ
+
+
+def pin_mlp_backward_autograd():
+    """The sharded backward (every rank, partials summed, gradient blocks assembled in rank
+    order) equals torch autograd through the unsplit float64 MLP gelu(X A) B."""
+    X, A, B, dZ = _mlp_bwd_inputs(34, 6, 8, 32)
+    tX, tA, tB = (torch.tensor(v, requires_grad=True) for v in (X, A, B))
+    Z = TF.gelu(tX @ tA, approximate="tanh") @ tB
+    (Z * _t(dZ)).sum().backward()
+    for world in (1, 2, 4, 8):
+        g = O.mlp_backward(X, A, B, dZ, world)
+        _close(g["dX"], tX.grad.numpy(), 1e-13, f"dX world={world}")
+        _close(g["dA"], tA.grad.numpy(), 1e-13, f"dA world={world}")
+        _close(g["dB"], tB.grad.numpy(), 1e-13, f"dB world={world}")
+
+
+def pin_mlp_backward_finite_difference():
+    """Brute force: central differences of the loss sum(dZ * Z), with Z the sum of the
+    oracle's forward shard partials, in single entries of X, A and B."""
+    X, A, B, dZ = _mlp_bwd_inputs(35, 3, 4, 8)
+    world = 2
+
+    def loss(X_, A_, B_):
+        Z = O.reduce_partials([O.mlp_shard(X_, A_, B_, r, world) for r in range(world)])
+        return float(np.sum(dZ * Z))
+
+    g = O.mlp_backward(X, A, B, dZ, world)
+    h = 1e-6
+    for name, M, idx in (("X", X, (1, 2)), ("X", X, (2, 0)), ("A", A, (0, 5)), ("A", A, (3, 1)),
+                         ("B", B, (6, 3)), ("B", B, (2, 0))):
+        Mp, Mm = M.copy(), M.copy()
+        Mp[idx] += h
+        Mm[idx] -= h
+        args_p = {"X": X, "A": A, "B": B}
+        args_m = dict(args_p)
+        args_p[name], args_m[name] = Mp, Mm
+        fd = (loss(args_p["X"], args_p["A"], args_p["B"])
+              - loss(args_m["X"], args_m["A"], args_m["B"])) / (2 * h)
+        got = g["d" + name][idx]
+        assert abs(fd - got) <= 1e-7 * max(1.0, abs(fd)), f"d{name}{idx}: {got} vs {fd}"
+
+
 # ----------------------------------------------------------------------------- accounting
 def pin_byte_accounting_golden():
     vals = {}

@@ -32,10 +32,12 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", src)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_head_shard",
-              "tp_partial_reduce_residual_ln", "tp_attn_workspace_bytes", "tp_status_string"):
+              "tp_partial_reduce_residual_ln", "tp_attn_workspace_bytes", "tp_status_string",
+              "tp_partial_reduce_scatter_residual_ln", "tp_col_linear_gelu_save",
+              "tp_row_linear_backward", "tp_col_linear_backward"):
         assert n in names
 
 
@@ -101,6 +103,35 @@ def rs(tp, **kw):
     return tp.lib.tp_partial_reduce_scatter_residual_ln(
         a["parts"], a["n"], a["stride"], a["res"], a["g"], a["b"], a["eps"], a["h"], a["y"],
         a["rows"], a["H"], a["rank"], a["world"], a["dtype"], a["stream"])
+
+
+def cols(tp, **kw):
+    a = dict(X=P, W=P, Y=P, ldy=512, U=P, ldu=512, seq=64, H=256, N=1024, rank=1, world=2,
+             dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_col_linear_gelu_save(a["X"], a["W"], a["Y"], a["ldy"], a["U"], a["ldu"],
+                                          a["seq"], a["H"], a["N"], a["rank"], a["world"],
+                                          a["dtype"], a["stream"])
+
+
+def rowb(tp, **kw):
+    a = dict(dZ=P, W=P, Y=P, ldy=512, U=P, ldu=512, dY=P, ld_dy=512, dW=P, ld_dw=256, seq=64,
+             K=1024, N=256, rank=1, world=2, act=tp.TP_ACT_GELU_TANH, acc=0, dtype=tp.TP_BF16,
+             stream=None)
+    a.update(kw)
+    return tp.lib.tp_row_linear_backward(a["dZ"], a["W"], a["Y"], a["ldy"], a["U"], a["ldu"],
+                                         a["dY"], a["ld_dy"], a["dW"], a["ld_dw"], a["seq"],
+                                         a["K"], a["N"], a["rank"], a["world"], a["act"], a["acc"],
+                                         a["dtype"], a["stream"])
+
+
+def colb(tp, **kw):
+    a = dict(X=P, W=P, dU=P, ldu=512, dX=P, dW=P, ld_dw=512, seq=64, H=256, N=1024, rank=0,
+             world=2, acc=1, dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_col_linear_backward(a["X"], a["W"], a["dU"], a["ldu"], a["dX"], a["dW"],
+                                         a["ld_dw"], a["seq"], a["H"], a["N"], a["rank"],
+                                         a["world"], a["acc"], a["dtype"], a["stream"])
 
 
 CASES = [
@@ -177,6 +208,52 @@ CASES = [
     ("scatter stride too small", rs, dict(stride=64 * 256 - 8), "TP_ERR_SHAPE"),
     ("scatter H % 8", rs, dict(H=260, stride=64 * 260), "TP_ERR_ALIGN"),
     ("scatter misaligned h", rs, dict(h=P + 4), "TP_ERR_ALIGN"),
+    # column-parallel linear keeping the pre-activation
+    ("save null U", cols, dict(U=None), "TP_ERR_NULL"),
+    ("save null Y", cols, dict(Y=None), "TP_ERR_NULL"),
+    ("save f32", cols, dict(dtype=0), "TP_ERR_DTYPE"),
+    ("save rank = world", cols, dict(rank=2), "TP_ERR_RANK"),
+    ("save ldu < N/world", cols, dict(ldu=504), "TP_ERR_SHAPE"),
+    ("save N % world", cols, dict(world=3, rank=0, ldy=1024, ldu=1024), "TP_ERR_DIVISIBLE"),
+    ("save ldu % 8", cols, dict(ldu=516), "TP_ERR_ALIGN"),
+    ("save misaligned U", cols, dict(U=P + 8), "TP_ERR_ALIGN"),
+    # row-parallel backward
+    ("rowb null dZ", rowb, dict(dZ=None), "TP_ERR_NULL"),
+    ("rowb null W", rowb, dict(W=None), "TP_ERR_NULL"),
+    ("rowb no output", rowb, dict(dY=None, dW=None), "TP_ERR_NULL"),
+    ("rowb dW without Y", rowb, dict(Y=None), "TP_ERR_NULL"),
+    ("rowb gelu without U", rowb, dict(U=None), "TP_ERR_NULL"),
+    ("rowb f32", rowb, dict(dtype=0), "TP_ERR_DTYPE"),
+    ("rowb bad act", rowb, dict(act=2), "TP_ERR_DTYPE"),
+    ("rowb rank < 0", rowb, dict(rank=-1), "TP_ERR_RANK"),
+    ("rowb seq 0", rowb, dict(seq=0), "TP_ERR_SHAPE"),
+    ("rowb seq beyond 2^30", rowb, dict(seq=(1 << 30) + 8), "TP_ERR_SHAPE"),
+    ("rowb K % world", rowb, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("rowb ld_dy < K/world", rowb, dict(ld_dy=504), "TP_ERR_SHAPE"),
+    ("rowb ldu < K/world", rowb, dict(ldu=504), "TP_ERR_SHAPE"),
+    ("rowb ldy < K/world", rowb, dict(ldy=504), "TP_ERR_SHAPE"),
+    ("rowb ld_dw < N", rowb, dict(ld_dw=248), "TP_ERR_SHAPE"),
+    ("rowb N beyond 2^21", rowb, dict(N=(1 << 21) + 8, ld_dw=(1 << 21) + 8), "TP_ERR_SHAPE"),
+    ("rowb ldy beyond 2^21", rowb, dict(ldy=(1 << 21) + 8), "TP_ERR_SHAPE"),
+    ("rowb misaligned dW", rowb, dict(dW=P + 4), "TP_ERR_ALIGN"),
+    ("rowb misaligned U", rowb, dict(U=P + 2), "TP_ERR_ALIGN"),
+    ("rowb K/world % 8", rowb, dict(K=1032, ldy=520, ldu=520, ld_dy=520), "TP_ERR_ALIGN"),
+    ("rowb ld_dw % 8", rowb, dict(ld_dw=260), "TP_ERR_ALIGN"),
+    # column-parallel backward
+    ("colb null X", colb, dict(X=None), "TP_ERR_NULL"),
+    ("colb null dU", colb, dict(dU=None), "TP_ERR_NULL"),
+    ("colb no output", colb, dict(dX=None, dW=None), "TP_ERR_NULL"),
+    ("colb f32", colb, dict(dtype=0), "TP_ERR_DTYPE"),
+    ("colb world 0", colb, dict(world=0), "TP_ERR_RANK"),
+    ("colb H 0", colb, dict(H=0), "TP_ERR_SHAPE"),
+    ("colb N % world", colb, dict(world=3), "TP_ERR_DIVISIBLE"),
+    ("colb ldu < N/world", colb, dict(ldu=504), "TP_ERR_SHAPE"),
+    ("colb ld_dw < N/world", colb, dict(ld_dw=504), "TP_ERR_SHAPE"),
+    ("colb H beyond 2^21", colb, dict(H=(1 << 21) + 8), "TP_ERR_SHAPE"),
+    ("colb N beyond 2^21", colb, dict(N=(1 << 21) + 16, ldu=(1 << 20) + 8, ld_dw=(1 << 20) + 8),
+     "TP_ERR_SHAPE"),
+    ("colb misaligned dX", colb, dict(dX=P + 8), "TP_ERR_ALIGN"),
+    ("colb ldu % 8", colb, dict(ldu=516), "TP_ERR_ALIGN"),
 ]
 
 

@@ -144,6 +144,53 @@ def _gather_rows_reversed(blocks):
     return _orig["concat_rows"](list(blocks)[::-1])
 
 
+def _gelu_grad_first_term_only(x):
+    x = np.asarray(x, np.float64)
+    return 0.5 * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _gelu_grad_minus(x):
+    x = np.asarray(x, np.float64)
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (x + 0.044715 * x ** 3))
+    return 0.5 * (1.0 + t) - 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x)
+
+
+def _gelu_grad_no_three(x):
+    x = np.asarray(x, np.float64)
+    c = math.sqrt(2.0 / math.pi)
+    t = np.tanh(c * (x + 0.044715 * x ** 3))
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 0.044715 * x * x)
+
+
+def _row_bwd_no_act(dZ, Y, W, rank, world, U=None, act="none"):
+    return _orig["row_linear_backward"](dZ, Y, W, rank, world)
+
+
+def _row_bwd_act_of_output(dZ, Y, W, rank, world, U=None, act="none"):
+    return _orig["row_linear_backward"](dZ, Y, W, rank, world, Y, act)
+
+
+def _row_bwd_rank0_block(dZ, Y, W, rank, world, U=None, act="none"):
+    return _orig["row_linear_backward"](dZ, Y, W, 0, world, U, act)
+
+
+def _row_bwd_wgrad_transposed(dZ, Y, W, rank, world, U=None, act="none"):
+    dY, dW = _orig["row_linear_backward"](dZ, Y, W, rank, world, U, act)
+    return dY, np.asarray(dZ, np.float64).T @ np.asarray(Y, np.float64)
+
+
+def _col_bwd_rank0_block(dU, X, W, rank, world):
+    return _orig["col_linear_backward"](dU, X, W, 0, world)
+
+
+def _col_bwd_wgrad_uses_x_block(dU, X, W, rank, world):
+    dXp, _ = _orig["col_linear_backward"](dU, X, W, rank, world)
+    X = np.asarray(X, np.float64)
+    n = np.asarray(dU).shape[1]
+    return dXp, X[:, :n].T @ np.asarray(dU, np.float64) if X.shape[1] >= n else X.T @ dU
+
+
 MUTATIONS = {
     "shard_off_by_one": ("shard_range", _shard_off_by_one),
     "shard_reversed_ranks": ("shard_range", _shard_reversed),
@@ -168,6 +215,15 @@ MUTATIONS = {
     "scatter_takes_rank0_rows": ("reduce_scatter_rows", _scatter_rank0_block),
     "scatter_residual_not_sliced": ("reduce_scatter_residual_layernorm", _scatter_residual_unsliced),
     "gather_rows_reversed": ("concat_rows", _gather_rows_reversed),
+    "gelu_grad_first_term_only": ("gelu_tanh_grad", _gelu_grad_first_term_only),
+    "gelu_grad_wrong_sign": ("gelu_tanh_grad", _gelu_grad_minus),
+    "gelu_grad_missing_three": ("gelu_tanh_grad", _gelu_grad_no_three),
+    "row_bwd_drops_act_factor": ("row_linear_backward", _row_bwd_no_act),
+    "row_bwd_act_at_output": ("row_linear_backward", _row_bwd_act_of_output),
+    "row_bwd_rank0_weight_block": ("row_linear_backward", _row_bwd_rank0_block),
+    "row_bwd_weight_grad_transposed": ("row_linear_backward", _row_bwd_wgrad_transposed),
+    "col_bwd_rank0_weight_block": ("col_linear_backward", _col_bwd_rank0_block),
+    "col_bwd_weight_grad_x_block": ("col_linear_backward", _col_bwd_wgrad_uses_x_block),
 }
 
 

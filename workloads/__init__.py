@@ -11,4 +11,5 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     generate,
+    output_gradient,
 )

@@ -96,6 +96,14 @@ def generate(cfg: Config, only: Optional[set] = None,
     return out
 
 
+def output_gradient(cfg: Config, threads: Optional[int] = None) -> HostTensor:
+    """The gradient dZ [T, H] arriving at the layer's output in the backward pass: N(0, 1)
+    in the io dtype, from its own stream (the draw index after the forward inputs)."""
+    shape = (cfg.tokens, cfg.hidden)
+    arr = _draw(cfg.seed, len(cfg.draws()), shape, 0, cfg.dtype, threads)
+    return HostTensor("dZ", cfg.dtype, shape, arr)
+
+
 def random_affine(cfg: Config, seed: int) -> Dict[str, HostTensor]:
     """Non-trivial LayerNorm gamma/beta for extra coverage (gamma ~ 1 + 0.5 N(0,1),
     beta ~ 0.5 N(0,1))."""
