@@ -17,8 +17,10 @@ TFLOP/s.  Per-kernel durations come from HIP events recorded on the launch strea
 the timed region; the roofline object reports the dominant GEMM (the column-parallel
 GEMM + GeLU of the MLP).  The CPU baseline times the float64 oracle on a bounded row
 sample of the same workload on this host.  After the timed steps, the sequence-parallel
-form of the epilogue (each rank's reduce-scatter of its 1024 rows) is timed on its own and
-reported beside the step, outside `value`.
+form of the epilogue (each rank's reduce-scatter of its 1024 rows) and the backward pass of
+the MLP pair (the four gradient products of every rank and the reduce of the input-gradient
+partials; --no-backward skips it) are timed on their own and reported beside the step,
+outside `value`.
 """
 from __future__ import annotations
 
@@ -101,12 +103,73 @@ def cpu_baseline(cfg, t, qkv_vals) -> dict:
                        f"{flops / 1e9:.0f} GFLOP in {dt:.1f} s")}
 
 
+def mlp_backward_leg(cfg, t, blk, stream) -> dict:
+    """Backward of the block's MLP pair (outside the timed forward step): every rank's four
+    backward products, dY = dZ.W2_r^T with GeLU' fused, dW2_r = Y_r^T.dZ, dX_r = dU_r.W1_r^T,
+    dW1_r = X^T.dU_r, then the reduce of the 8 input-gradient partials.  One untimed pass,
+    then two timed passes; each product is timed on its own with HIP events on its stream."""
+    import torch
+    from megatron_tensor_transformer_linear_amd import pipeline as pl
+    from workloads import output_gradient
+
+    dev = torch.device("cuda:0")
+    dZ = pl.to_device(output_gradient(cfg).data, "bf16", dev)
+    trn = pl.MLPTrainShard(blk.X, blk.W1, blk.W2, dZ, cfg.world)
+    trn.forward()  # saves U_r and Y_r of every rank
+    legs = {"dY": lambda r: trn.backward_row(r, True, False),
+            "dW2": lambda r: trn.backward_row(r, False, True),
+            "dX_part": lambda r: trn.backward_col(r, True, False),
+            "dW1": lambda r: trn.backward_col(r, False, True)}
+    ev = {k: [] for k in list(legs) + ["reduce_dX"]}
+    for it in range(3):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for r in range(cfg.world):
+            for k, fn in legs.items():
+                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s_.record(stream)
+                fn(r)
+                e_.record(stream)
+                if it > 0:
+                    ev[k].append((s_, e_))
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        trn.reduce_dx()
+        e_.record(stream)
+        if it > 0:
+            ev["reduce_dX"].append((s_, e_))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if it > 0:
+            ev.setdefault("pass", []).append((s0, e0))
+    torch.cuda.synchronize()
+    T, H, fl = cfg.tokens, cfg.hidden, cfg.ffn // cfg.world
+    gemm_flops = 2.0 * T * H * fl  # each of the four products
+    out = {"what": "backward of the MLP pair, 8 ranks: dY (NT, GeLU' fused), dW2 (TN), "
+                   "dX partial (NT), dW1 (TN), reduce of the dX partials",
+           "gemm_gflop_per_rank": round(4 * gemm_flops / 1e9, 1)}
+    for k in legs:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[k]]))
+        out[k] = {"avg_ms": round(ms, 4), "tflops": round(gemm_flops / ms / 1e9, 1)}
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev["reduce_dX"]]))
+    nbytes = reduce_bytes(T, H, cfg.world, "bf16", residual=False, h_out=True, y_out=False)
+    out["reduce_dX"] = {"avg_ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                        "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev["pass"]]))
+    out["pass_ms"] = round(ms, 3)
+    out["pass_tflops"] = round(cfg.world * 4 * gemm_flops / ms / 1e9, 1)
+    del trn
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass measurement of the MLP pair")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain copy kernel over MIB mebibytes (reads and writes "
                          "MIB each), the known-size reference for HBM byte counters")
@@ -271,6 +334,8 @@ def main() -> int:
         "hbm_frac": round(sp_bytes / sp_ms / 1e6 / PEAK_HBM_GBS, 3),
         "all_ranks_ms": round(sp_ms * cfg.world, 4),
     }
+    if not args.no_backward:
+        result["mlp_backward"] = mlp_backward_leg(cfg, t, blk, stream)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(cfg, t, np.hstack(

@@ -138,16 +138,19 @@ class MLPTrainShard:
         tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, None, None, None,
                                          0.0, self.Z, None, self.T, self.H, tp.TP_F32, self.stream)
 
-    def backward_row(self, r: int):
+    def backward_row(self, r: int, input_grad: bool = True, weight_grad: bool = True):
         tp.tp_row_linear_backward(self.dZ, self.B, self.Y[r], self.fl, self.U[r], self.fl,
-                                  self.dU[r], self.fl, self.dB[r * self.fl:], self.H, self.T,
+                                  self.dU[r] if input_grad else None, self.fl,
+                                  self.dB[r * self.fl:] if weight_grad else None, self.H, self.T,
                                   self.F, self.H, r, self.P, tp.TP_ACT_GELU_TANH,
                                   int(self.accumulate), tp.TP_BF16, self.stream)
 
-    def backward_col(self, r: int):
-        tp.tp_col_linear_backward(self.X, self.A, self.dU[r], self.fl, self.dXparts[r],
-                                  self.dA[:, r * self.fl:], self.F, self.T, self.H, self.F, r,
-                                  self.P, int(self.accumulate), tp.TP_BF16, self.stream)
+    def backward_col(self, r: int, input_grad: bool = True, weight_grad: bool = True):
+        tp.tp_col_linear_backward(self.X, self.A, self.dU[r], self.fl,
+                                  self.dXparts[r] if input_grad else None,
+                                  self.dA[:, r * self.fl:] if weight_grad else None, self.F,
+                                  self.T, self.H, self.F, r, self.P, int(self.accumulate),
+                                  tp.TP_BF16, self.stream)
 
     def reduce_dx(self):
         tp.tp_partial_reduce_residual_ln(self.dXparts, self.P, self.T * self.H, None, None, None,
