@@ -113,13 +113,16 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, int64_t bytes) 
 // voff + soff, land at LDS address lds_base + IMM + 16 i.  Issued through inline assembly
 // so that the compiler does not order LDS reads after it with a full vector-memory wait;
 // completion is tracked by the explicit vmcnt waits of the K loop.  M0 (the LDS address of
-// the load) is set here and used by nothing else in the kernel.
+// the load) is set here and used by nothing else in the kernel.  The s_add_u32 also writes
+// SCC, so SCC is declared clobbered: without it the compiler may keep a comparison result
+// in SCC across this statement (seen on a K-tail bound test, which then read the carry of
+// the add and loaded past K).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <uint32_t IMM>
 __device__ __forceinline__ void dma16(uint32_t lds_base, uint32_t voff, i32x4_t rsrc, uint32_t soff) {
   asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, %4 offen lds"
-               :: "s"(lds_base), "i"(IMM), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+               :: "s"(lds_base), "i"(IMM), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 
@@ -129,6 +132,15 @@ __device__ __forceinline__ bf16x8_t ds_read_tr_pair(const char* p, int second_of
   i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lp + second_offset));
   i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// The value unchanged, but opaque to the optimiser: a K-contiguous operand's per-lane offsets
+// are the same for every tile, and without this the k-bound selections of the last K steps
+// are hoisted out of the tile loop, spilled, and reloaded with a wait that also drains the
+// stage loads in flight.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}).
@@ -182,6 +194,15 @@ __device__ __forceinline__ void tile_coords(int bid, int tm, int tn, int& tile_m
   tile_n = w / gsz;
 }
 
+// K-contiguous operands are staged a pair of K steps at a time (see the kernel); false stages
+// them one K step per ring slot like the other operands.
+constexpr bool KC_PAIRS = true;
+
+// Row permutation of the 16-byte chunks of a 128-byte LDS row of a paired operand: the 16
+// lanes of a read group address 16 consecutive rows, two per 256 bytes, and (r >> 1) & 7
+// sends them to 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_p(int row) { return (row >> 1) & 7; }
+
 // Stage geometry of one operand with R rows (K-contiguous, KC) or R columns (M- or
 // N-contiguous) per tile.
 template <int R, bool KC>
@@ -198,6 +219,17 @@ template <int BM, int BN, int NST, int EPI, int LAY>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   constexpr bool A_KC = (LAY & LAY_TN) == 0;  // A stored [M, K]
   constexpr bool B_KC = (LAY & LAY_NT) != 0;  // B stored as B^T [N, K]
+  // A K-contiguous operand is staged a pair of K steps at a time: pair p (steps 2p, 2p+1)
+  // fills that operand's share of ring slots 2p and 2p+1 (mod NST), the first half of its
+  // rows in slot 2p and the second half in slot 2p+1, each row as 128 contiguous bytes
+  // (64 k).  A load then fetches whole 128-byte lines, where one K step of a row is half a
+  // line: on MI355X that halves the operand's L1-to-L2 requests, and the address path had
+  // stalled on them (a product whose operands are both K-contiguous ran 17 % slower than
+  // the same product with neither).  Each wave's MFMA rows are one half, so a wave reads
+  // one slot of the pair.
+  constexpr bool A_PAIR = A_KC && KC_PAIRS;
+  constexpr bool B_PAIR = B_KC && KC_PAIRS;
+  static_assert(!(A_PAIR || B_PAIR) || NST == 4, "paired staging is scheduled for a 4-slot ring");
   using SA = OperandStage<BM, A_KC>;
   using SB = OperandStage<BN, B_KC>;
   constexpr int WM = BM / 2;                      // rows per wave
@@ -207,8 +239,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   constexpr int A_BYTES = SA::BYTES;              // A's share of a stage, first
   constexpr int STAGE = A_BYTES + SB::BYTES;
   constexpr int A_LD = SA::LD;                    // load instructions per wave per stage
-  constexpr int B_LD = SB::LD;
-  constexpr int LPS = A_LD + B_LD;
+  constexpr int B_LD = SB::LD;                    // (paired: per half pair, the same count)
+  // Per wave: LM loads per stage of the operands staged one step at a time (LMH of them go
+  // out with the stage's first half), LK loads per half pair of the paired operands.  Load
+  // items are numbered A first: single-step items [0, LA_M) are A's, pair items [0, LA_K).
+  constexpr int LA_M = A_PAIR ? 0 : A_LD;
+  constexpr int LM = LA_M + (B_PAIR ? 0 : B_LD);
+  constexpr int LMH = LM / 2;
+  constexpr int LA_K = A_PAIR ? A_LD : 0;
+  constexpr int LK = LA_K + (B_PAIR ? B_LD : 0);
   static_assert(BN == 256 || BN == 192 || BN == 128, "tile width");
   static_assert(BM == 256 || BM == 128, "tile height");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
@@ -229,29 +268,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const int64_t lda = g.lda, ldb = g.ldb;
 
   // ---- per-lane source offsets of one tile's direct-to-LDS loads.  A K-contiguous operand's
-  // instruction i of wave wv fills rows 16 (LD wv + i) .. +15 of its share, 4 lanes a row,
-  // from a resource spanning the tile's rows (k past K is sent out of range per load).  A
-  // contiguous-along-M/N operand's instruction i fills k-rows RPI (LD wv + i) ..; its
-  // resource is re-based at every stage (see dma_item) and columns past the end get an
-  // out-of-range offset.  A tile index past the end loads zeros throughout.
+  // instruction i of wave wv fills rows 16 (LD wv + i) .. +15 of its share, 4 lanes a row
+  // (paired: rows 8 (LD wv + i) .. +7 of a half, 8 lanes a row), from a resource spanning
+  // the tile's rows (k past K is sent out of range per load).  A contiguous-along-M/N
+  // operand's instruction i fills k-rows RPI (LD wv + i) ..; its resource is re-based at
+  // every stage (see dma_item) and columns past the end get an out-of-range offset.  A tile
+  // index past the end loads zeros throughout.
   struct TileLoads {
     i32x4_t rsrc_a, rsrc_b;
     uint32_t a_off[A_LD];
-    int a_k[A_LD];
     uint32_t b_off[B_LD];
-    int b_k[B_LD];
   };
-  auto kc_loads = [&](auto SC, const bf16_t* base, int64_t rows, int64_t ld, i32x4_t& rsrc,
-                      uint32_t* off, int* kk) {
+  // Row and first k (relative to the stage or pair) of lane `lane`'s 16 bytes in load
+  // instruction i of a K-contiguous operand (PR: paired).
+  auto kc_row = [&](auto SC, auto PC, int i) {
+    using S = decltype(SC);
+    return decltype(PC)::value ? 8 * (S::LD * wv + i) + (lane >> 3) : 16 * (S::LD * wv + i) + (lane >> 2);
+  };
+  auto kc_k = [&](auto SC, auto PC, int i) {
+    const int row = kc_row(SC, PC, i);
+    return 8 * (decltype(PC)::value ? (lane & 7) ^ swz_p(row) : (lane & 3) ^ swz_a(row));
+  };
+  // Byte offsets are formed in 32 bits: a row index below 256 times a leading dimension of
+  // at most 2^21 elements (K-contiguous), or a k-row below 32 times at most 2^23, plus a
+  // column below the leading dimension, stays under 2^30 bytes.
+  auto kc_loads = [&](auto SC, auto PC, const bf16_t* base, int64_t rows, int64_t ld,
+                      i32x4_t& rsrc, uint32_t* off) {
     using S = decltype(SC);
     rsrc = buffer_rsrc(base, rows * ld * 2);
+    const uint32_t ld32 = (uint32_t)ld;
 #pragma unroll
-    for (int i = 0; i < S::LD; ++i) {
-      const int row = 16 * (S::LD * wv + i) + (lane >> 2);
-      const int c = (lane & 3) ^ swz_a(row);
-      kk[i] = 8 * c;
-      off[i] = (uint32_t)((row * ld + 8 * c) * 2);
-    }
+    for (int i = 0; i < S::LD; ++i)
+      off[i] = ((uint32_t)kc_row(SC, PC, i) * ld32 + (uint32_t)kc_k(SC, PC, i)) * 2u;
   };
   auto tile_loads = [&](int t, TileLoads& d) {
     int tile_m = 0, tile_n = 0;
@@ -259,7 +307,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     if (live) tile_coords(t, tm, tn, tile_m, tile_n);
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
     if constexpr (A_KC) {
-      kc_loads(SA{}, A + m0 * lda, live ? min((int64_t)BM, M - m0) : 0, lda, d.rsrc_a, d.a_off, d.a_k);
+      kc_loads(SA{}, std::integral_constant<bool, A_PAIR>{}, A + m0 * lda,
+               live ? min((int64_t)BM, M - m0) : 0, lda, d.rsrc_a, d.a_off);
     } else {
 #pragma unroll
       for (int i = 0; i < A_LD; ++i) {
@@ -267,12 +316,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         const int j = (lane % SA::CPR) ^ swz_b(krow);
         const int64_t m = m0 + 8 * j;
         const bool ok = live && 8 * j < BM && m < M;
-        d.a_off[i] = ok ? (uint32_t)((krow * lda + m) * 2) : OOB;
+        d.a_off[i] = ok ? ((uint32_t)krow * (uint32_t)lda + (uint32_t)m) * 2u : OOB;
       }
     }
     if constexpr (B_KC) {
-      kc_loads(SB{}, B + (g.n_off + n0) * ldb, live ? min((int64_t)BN, N - n0) : 0, ldb, d.rsrc_b,
-               d.b_off, d.b_k);
+      kc_loads(SB{}, std::integral_constant<bool, B_PAIR>{}, B + (g.n_off + n0) * ldb,
+               live ? min((int64_t)BN, N - n0) : 0, ldb, d.rsrc_b, d.b_off);
     } else {
 #pragma unroll
       for (int i = 0; i < B_LD; ++i) {
@@ -280,9 +329,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         const int j = (lane % SB::CPR) ^ swz_b(krow);
         const int64_t nlog = n0 + 8 * j;
         const bool ok = live && 8 * j < BN && nlog < N;
-        const int64_t nb = g.n_off + nlog;  // logical column of the whole B operand
-        const int64_t col = (nb / g.b_blk) * g.b_blk_stride + (nb % g.b_blk);
-        d.b_off[i] = ok ? (uint32_t)((krow * ldb + col) * 2) : OOB;
+        // logical column of the whole B operand (below 2^23), then its physical column
+        const uint32_t nb = (uint32_t)(g.n_off + nlog), blk = (uint32_t)g.b_blk;
+        const uint32_t col = (nb / blk) * (uint32_t)g.b_blk_stride + nb % blk;
+        d.b_off[i] = ok ? ((uint32_t)krow * (uint32_t)ldb + col) * 2u : OOB;
       }
     }
   };
@@ -292,21 +342,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const int grp = lane >> 4, li = lane & 15, q = li & 3, s = li >> 2;
   // K-contiguous share: sub-step ks of this wave's rows w0 + 0..31 (block i adds i * 2048).
   auto kc_rd = [&](int w0, int ks) { return (w0 + r32) * 64 + (((2 * ks + kh) ^ swz_a(r32)) * 16); };
+  // Paired K-contiguous share: this wave's half w of the rows (slot w of the pair), K step
+  // parity par, sub-step ks (block i adds i * 4096; the pair's first slot is added at the
+  // read).
+  auto kp_rd = [&](int w, int par, int ks) {
+    return w * STAGE + r32 * 128 + (((4 * par + 2 * ks + kh) ^ swz_p(r32)) * 16);
+  };
   // Contiguous-along-M/N share: block j of this wave's columns w0.. (sub-step ks adds
   // 16 k-rows).
   auto mn_rd = [&](int w0, int j, int pitch) {
     const int chunk = w0 / 8 + 4 * j + 2 * (grp & 1) + (q >> 1);
     return (8 * (grp >> 1) + s) * pitch + ((chunk ^ swz_b(s)) * 16) + (q & 1) * 8;
   };
-  int a_rd[A_KC ? 2 : MI], b_rd[B_KC ? 2 : NJ];
-  if constexpr (A_KC) {
+  int a_rd[A_PAIR ? 4 : A_KC ? 2 : MI], b_rd[B_PAIR ? 4 : B_KC ? 2 : NJ];
+  if constexpr (A_PAIR) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a_rd[q] = kp_rd(wm, q >> 1, q & 1);
+  } else if constexpr (A_KC) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) a_rd[ks] = kc_rd(wm * WM, ks);
   } else {
 #pragma unroll
     for (int i = 0; i < MI; ++i) a_rd[i] = mn_rd(wm * WM, i, SA::PITCH);
   }
-  if constexpr (B_KC) {
+  if constexpr (B_PAIR) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b_rd[q] = A_BYTES + kp_rd(wn, q >> 1, q & 1);
+  } else if constexpr (B_KC) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) b_rd[ks] = A_BYTES + kc_rd(wn * WN, ks);
   } else {
@@ -354,30 +416,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   // (t < MI: A block t, else B block t - MI).
   auto read_item = [&](int buf, int ks, int slot, int t) {
     const char* sb = smem + buf * STAGE;
+    const char* sp = smem + (buf & ~1) * STAGE;  // first slot of the pair holding stage buf
     if (t < MI) {
-      if constexpr (A_KC) fa[slot][t] = *(const bf16x8_t*)(sb + a_rd[ks] + t * 32 * 64);
+      if constexpr (A_PAIR) fa[slot][t] = *(const bf16x8_t*)(sp + a_rd[2 * (buf & 1) + ks] + t * 32 * 128);
+      else if constexpr (A_KC) fa[slot][t] = *(const bf16x8_t*)(sb + a_rd[ks] + t * 32 * 64);
       else fa[slot][t] = ds_read_tr_pair(sb + a_rd[t] + ks * 16 * SA::PITCH, 4 * SA::PITCH);
     } else {
       const int j = t - MI;
-      if constexpr (B_KC) fb[slot][j] = *(const bf16x8_t*)(sb + b_rd[ks] + j * 32 * 64);
+      if constexpr (B_PAIR) fb[slot][j] = *(const bf16x8_t*)(sp + b_rd[2 * (buf & 1) + ks] + j * 32 * 128);
+      else if constexpr (B_KC) fb[slot][j] = *(const bf16x8_t*)(sb + b_rd[ks] + j * 32 * 64);
       else fb[slot][j] = ds_read_tr_pair(sb + b_rd[j] + ks * 16 * SB::PITCH, 4 * SB::PITCH);
     }
   };
-  // Load item U of stage kd (counted within the tile whose loads `d` describes) into buffer
-  // BUF (U < A_LD: an A load, else a B load).  Parts of a stage past K, and whole stages
-  // past K, come back as zeros (out-of-range offsets or an empty range), so the K loop can
-  // run whole groups of NST steps.  A contiguous-along-M/N operand's resource is re-based at
-  // every stage so that its range check alone bounds the k-rows read.
+  // Single-step load item U of stage kd (counted within the tile whose loads `d` describes)
+  // into buffer BUF (U < LA_M: an A load, else a B load).  Parts of a stage past K, and
+  // whole stages past K, come back as zeros (out-of-range offsets or an empty range), so the
+  // K loop can run whole groups of NST steps.  A contiguous-along-M/N operand's resource is
+  // re-based at every stage so that its range check alone bounds the k-rows read; a
+  // K-contiguous operand's k bound is tested per lane, in a step (or pair) that reaches past K
+  // (the test is wave-uniform otherwise), and only in loads issued in the last two groups of
+  // K steps of a tile (CHK): an earlier load's stage ends at or before K.
   const int Ki = (int)K;                       // K < 2^31 (bounded by the leading dimensions)
   const int lda2 = (int)(lda * 2), ldb2 = (int)(ldb * 2);  // bytes per stored row
   const char* const Abytes = (const char*)A;
   const char* const Bbytes = (const char*)B;
-  auto dma_item = [&](auto BUFC, auto UC, const TileLoads& d, int kd) {
+  auto dma_item = [&](auto CHKC, auto BUFC, auto UC, const TileLoads& d, int kd) {
+    constexpr bool CHK = decltype(CHKC)::value;
     constexpr int BUF = decltype(BUFC)::value, U = decltype(UC)::value;
     const int k0 = kd * BK;
-    if constexpr (U < A_LD) {
+    if constexpr (U < LA_M) {
       if constexpr (A_KC) {
-        const uint32_t off = d.a_k[U] < Ki - k0 ? d.a_off[U] : OOB;
+        uint32_t off = d.a_off[U];
+        if constexpr (CHK) {
+          off = opaque(off);
+          if (k0 + BK > Ki && kc_k(SA{}, std::false_type{}, U) >= Ki - k0) off = OOB;
+        }
         dma16<BUF * STAGE + U * 1024>(lds_a, off, d.rsrc_a, (uint32_t)k0 * 2u);
       } else {
         const int k_rows = max(0, min(BK, Ki - k0));
@@ -385,9 +458,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         dma16<BUF * STAGE + U * 1024>(lds_a, d.a_off[U], rsrc, 0u);
       }
     } else {
-      constexpr int I = U - A_LD;
+      constexpr int I = U - LA_M;
       if constexpr (B_KC) {
-        const uint32_t off = d.b_k[I] < Ki - k0 ? d.b_off[I] : OOB;
+        uint32_t off = d.b_off[I];
+        if constexpr (CHK) {
+          off = opaque(off);
+          if (k0 + BK > Ki && kc_k(SB{}, std::false_type{}, I) >= Ki - k0) off = OOB;
+        }
         dma16<BUF * STAGE + I * 1024>(lds_b, off, d.rsrc_b, (uint32_t)k0 * 2u);
       } else {
         const int k_rows = max(0, min(BK, Ki - k0));
@@ -396,16 +473,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       }
     }
   };
+  // Pair load item U (U < LA_K: A, else B) of half H of pair kp into slot BUF (the pair's
+  // first slot + H); k past K comes back as zeros.  The second half's rows are reached by
+  // moving the resource's base by half a tile of rows (and shrinking its range to match),
+  // so both halves share the per-lane offsets.
+  const uint32_t a_half = (uint32_t)((BM / 2) * lda * 2), b_half = (uint32_t)((BN / 2) * ldb * 2);
+  auto second_half = [](i32x4_t r, uint32_t bytes) {
+    const uint64_t base = ((uint64_t)(uint32_t)r.y << 32 | (uint32_t)r.x) + bytes;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane((int)((uint32_t)r.z > bytes ? (uint32_t)r.z - bytes : 0u));
+    return r;
+  };
+  auto dma_pair = [&](auto CHKC, auto BUFC, auto HC, auto UC, const TileLoads& d, int kp) {
+    constexpr bool CHK = decltype(CHKC)::value;
+    constexpr int BUF = decltype(BUFC)::value, H = decltype(HC)::value, U = decltype(UC)::value;
+    const int k0 = kp * 2 * BK;
+    if constexpr (U < LA_K) {
+      uint32_t off = d.a_off[U];
+      if constexpr (CHK) {
+        off = opaque(off);
+        if (k0 + 2 * BK > Ki && kc_k(SA{}, std::true_type{}, U) >= Ki - k0) off = OOB;
+      }
+      dma16<BUF * STAGE + U * 1024>(lds_a, off, H ? second_half(d.rsrc_a, a_half) : d.rsrc_a,
+                                    (uint32_t)k0 * 2u);
+    } else {
+      constexpr int I = U - LA_K;
+      uint32_t off = d.b_off[I];
+      if constexpr (CHK) {
+        off = opaque(off);
+        if (k0 + 2 * BK > Ki && kc_k(SB{}, std::true_type{}, I) >= Ki - k0) off = OOB;
+      }
+      dma16<BUF * STAGE + I * 1024>(lds_b, off, H ? second_half(d.rsrc_b, b_half) : d.rsrc_b,
+                                    (uint32_t)k0 * 2u);
+    }
+  };
 
-  // One half-step: the NM MFMAs on fragment slot SLOT, with NR fragment reads (sub-step
-  // ks_read of buffer RBUF into slot read_slot) and the load items [LO, HI) of stage kd
-  // (into buffer DBUF) spread between them, each item fenced in place.
-  auto half_step = [&](auto SLOTC, auto LOC, auto HIC, auto RBUFC, int ks_read, int read_slot,
-                       auto DBUFC, const TileLoads& d, int kd) {
+  // One half-step: the NM MFMAs on fragment slot SLOT, with, spread between them and each
+  // fenced in place, NR fragment reads (sub-step ks_read of buffer RBUF into slot
+  // read_slot), then NK pair loads (half PH of pair kd / 2, into slot PBUF), then the
+  // single-step load items [LO, HI) of stage kd (into buffer DBUF).
+  auto half_step = [&](auto CHKC, auto SLOTC, auto LOC, auto HIC, auto NKC, auto PHC, auto PBUFC,
+                       auto RBUFC, int ks_read, int read_slot, auto DBUFC, const TileLoads& d,
+                       int kd) {
     constexpr int SLOT = decltype(SLOTC)::value;
     constexpr int LO = decltype(LOC)::value, HI = decltype(HIC)::value;
+    constexpr int NK = decltype(NKC)::value;
     constexpr int RBUF = decltype(RBUFC)::value;
-    constexpr int NITEM = NR + (HI - LO);
+    constexpr int NITEM = NR + NK + (HI - LO);
     static_for<NM>([&](auto MC) {
       constexpr int m = decltype(MC)::value;
       mfma(SLOT, m);
@@ -414,7 +529,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         constexpr int t = decltype(TC)::value;
         if constexpr (t * NM / NITEM == m) {
           if constexpr (t < NR) read_item(RBUF, ks_read, read_slot, t);
-          else dma_item(DBUFC, std::integral_constant<int, LO + t - NR>{}, d, kd);
+          else if constexpr (t < NR + NK)
+            dma_pair(CHKC, PBUFC, PHC, std::integral_constant<int, t - NR>{}, d, kd >> 1);
+          else dma_item(CHKC, DBUFC, std::integral_constant<int, LO + t - NR - NK>{}, d, kd);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -429,17 +546,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   // stage's sub-step 0 and the first half of the loads of the stage NST ahead (into buffer
   // S) between them.  Splitting each stage's loads over two half-steps keeps the four waves'
   // 1 KB loads from reaching the address unit in one burst.
-  constexpr int LH = LPS / 2;
-  auto step = [&](auto SC, const TileLoads& d1, int kd1, const TileLoads& d2, int kd2) {
+  // Paired operands: pair p's slots are free after the barrier of step 2p - 3 and must hold
+  // it by the barrier of step 2p - 1, so its first half goes out in the second half of step
+  // 2p - 3 (beside the first half of stage 2p + 1) and its second half in the first half of
+  // step 2p - 2 (beside the second half of stage 2p + 1): a half-step that loads an odd
+  // stage kd also loads a half of pair kd / 2.  The waits count this wave's loads issued
+  // after the last one the next step reads (pair loads go out before the single-step ones
+  // of the same half-step): at an even step that is the second half of stage S + 1, with
+  // 2 LM + 2 LK loads after it; at an odd step the second half of the pair holding S + 1,
+  // issued one step earlier, with 2 LM - LMH after it.
+  using std::integral_constant;
+  auto step = [&](auto SC, auto CHKC, const TileLoads& d1, int kd1, const TileLoads& d2, int kd2) {
     constexpr int S = decltype(SC)::value;
-    half_step(std::integral_constant<int, 0>{}, std::integral_constant<int, LH>{},
-              std::integral_constant<int, LPS>{}, SC, 1, 1,
-              std::integral_constant<int, (S + NST - 1) % NST>{}, d1, kd1);
-    wait_vmcnt_lgkm0<(NST - 2) * LPS>();
+    constexpr int SL1 = (S + NST - 1) % NST;                   // slot of stage kd1
+    constexpr bool P1 = LK > 0 && (S + NST - 1) % 2 == 1;     // kd1 odd
+    constexpr bool P2 = LK > 0 && S % 2 == 1;                 // kd2 = kd1 + 1 odd
+    constexpr int WAIT = LK == 0 ? (NST - 2) * LM : S % 2 == 0 ? 2 * LM + 2 * LK : 2 * LM - LMH;
+    half_step(CHKC, integral_constant<int, 0>{}, integral_constant<int, LMH>{}, integral_constant<int, LM>{},
+              integral_constant<int, P1 ? LK : 0>{}, integral_constant<int, 1>{},
+              integral_constant<int, (SL1 & ~1) + 1>{}, SC, 1, 1, integral_constant<int, SL1>{}, d1, kd1);
+    wait_vmcnt_lgkm0<WAIT>();
     lds_barrier();
-    half_step(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
-              std::integral_constant<int, LH>{}, std::integral_constant<int, (S + 1) % NST>{},
-              0, 0, SC, d2, kd2);
+    half_step(CHKC, integral_constant<int, 1>{}, integral_constant<int, 0>{}, integral_constant<int, LMH>{},
+              integral_constant<int, P2 ? LK : 0>{}, integral_constant<int, 0>{},
+              integral_constant<int, S & ~1>{}, integral_constant<int, (S + 1) % NST>{}, 0, 0, SC,
+              d2, kd2);
   };
 
   // ---- persistent loop over this workgroup's tiles t = blockIdx.x + i * gridDim.x.  The
@@ -449,12 +580,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   int t = blockIdx.x;
   tile_loads(t, cur);
   // prologue: stages 0 .. NST-2 and the first half of stage NST-1 in flight (its second
-  // half goes out in the first step), stage 0 landed, its first fragments read
+  // half goes out in the first step), pair 0 and the first half of pair 1 likewise, in the
+  // order pair 0, stage 0, stage 1, half of pair 1, stage 2, half of stage 3; stage 0 and
+  // pair 0 landed, their first fragments read
+  const std::true_type chk;
+  if constexpr (LK > 0) {
+    static_for<LK>([&](auto UC) { dma_pair(chk, integral_constant<int, 0>{}, integral_constant<int, 0>{}, UC, cur, 0); });
+    static_for<LK>([&](auto UC) { dma_pair(chk, integral_constant<int, 1>{}, integral_constant<int, 1>{}, UC, cur, 0); });
+  }
   static_for<NST - 1>([&](auto SC) {
-    static_for<LPS>([&](auto UC) { dma_item(SC, UC, cur, decltype(SC)::value); });
+    static_for<LM>([&](auto UC) { dma_item(chk, SC, UC, cur, decltype(SC)::value); });
+    if constexpr (LK > 0 && decltype(SC)::value == 1)
+      static_for<LK>([&](auto UC) { dma_pair(chk, integral_constant<int, 2>{}, integral_constant<int, 0>{}, UC, cur, 1); });
   });
-  static_for<LH>([&](auto UC) { dma_item(std::integral_constant<int, NST - 1>{}, UC, cur, NST - 1); });
-  wait_vmcnt<(NST - 2) * LPS + LH>();
+  static_for<LMH>([&](auto UC) { dma_item(chk, integral_constant<int, NST - 1>{}, UC, cur, NST - 1); });
+  wait_vmcnt<LK == 0 ? (NST - 2) * LM + LMH : 2 * LM + LK + LMH>();
   lds_barrier();
 #pragma unroll
   for (int r = 0; r < NR; ++r) read_item(0, 0, 0, r);
@@ -462,19 +602,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   const int64_t ldc = g.ldc;
   for (; t < nt; t += gridDim.x) {
     tile_loads(t + gridDim.x, nxt);
-    for (int gi = 0; gi < ng - 1; ++gi) {
+    // Groups 0 .. ng-3 load stages that end at or before K (unchecked); group ng-2 loads the
+    // last group's stages and the last group the next tile's first ones (checked).
+    auto group = [&](auto CHKC, int gi) {
       const int kt = gi * NST;
       static_for<NST>([&](auto SC) {
         constexpr int S = decltype(SC)::value;
-        step(SC, cur, kt + S + NST - 1, cur, kt + S + NST);
+        step(SC, CHKC, cur, kt + S + NST - 1, cur, kt + S + NST);
       });
-    }
+    };
+    for (int gi = 0; gi < ng - 2; ++gi) group(std::false_type{}, gi);
+    if (ng >= 2) group(chk, ng - 2);
     {  // last group: from its first second half on, the loads are the next tile's
       const int kt = (ng - 1) * NST;
-      step(std::integral_constant<int, 0>{}, cur, kt + NST - 1, nxt, 0);
+      step(std::integral_constant<int, 0>{}, chk, cur, kt + NST - 1, nxt, 0);
       static_for<NST - 1>([&](auto SC) {
         constexpr int S = decltype(SC)::value + 1;
-        step(std::integral_constant<int, S>{}, nxt, S - 1, nxt, S);
+        step(std::integral_constant<int, S>{}, chk, nxt, S - 1, nxt, S);
       });
     }
 
@@ -484,22 +628,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     const int64_t m_w = (int64_t)tile_m * BM + wm * WM, n_w = (int64_t)tile_n * BN + wn * WN;
     if constexpr (TRANS) {
       const int64_t row0 = m_w + (lane & 31), col0 = n_w + 4 * (lane >> 5);
+      // EPI_GELU_BWD: the tile's pre-activation values, all loaded before the first store.
+      // Loads and stores share one completion counter and complete out of order with
+      // respect to each other, so a load still pending behind a store can only be waited
+      // for with the store; one batch of loads and one wait keeps the stores from
+      // serialising the epilogue.
+      uint2 pre[EPI == EPI_GELU_BWD ? MI : 1][EPI == EPI_GELU_BWD ? NJ : 1][4];
+      if constexpr (EPI == EPI_GELU_BWD) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int64_t row = row0 + 32 * i;
-        // EPI_GELU_BWD: this row's pre-activation values, all loaded before the first store.
-        uint2 pre[EPI == EPI_GELU_BWD ? NJ : 1][4];
-        if constexpr (EPI == EPI_GELU_BWD) {
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-              const int64_t col = col0 + 32 * j + 8 * qq;
-              pre[j][qq] = row < M && col < N
-                               ? *(const uint2*)((const bf16_t*)g.aux + row * g.ldaux + col)
-                               : make_uint2(0u, 0u);
+              const int64_t row = row0 + 32 * i, col = col0 + 32 * j + 8 * qq;
+              pre[i][j][qq] = row < M && col < N
+                                  ? *(const uint2*)((const bf16_t*)g.aux + row * g.ldaux + col)
+                                  : make_uint2(0u, 0u);
             }
-        }
+        // One explicit wait for the whole batch: the bounds-checked stores below branch, and
+        // without it the compiler waits for every earlier store before each use of a value.
+        wait_vmcnt<0>();
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int64_t row = row0 + 32 * i;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -519,7 +672,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
                 v2 = gelu_tanh_fast(v2); v3 = gelu_tanh_fast(v3);
               }
               if constexpr (EPI == EPI_GELU_BWD) {
-                const uint2 p = pre[j][qq];
+                const uint2 p = pre[i][j][qq];
                 v0 *= gelu_tanh_grad_fast(__uint_as_float(p.x << 16));
                 v1 *= gelu_tanh_grad_fast(__uint_as_float(p.x & 0xFFFF0000u));
                 v2 *= gelu_tanh_grad_fast(__uint_as_float(p.y << 16));
@@ -537,21 +690,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       const int64_t row0 = m_w + 4 * (lane >> 5), col0 = n_w + (lane & 31);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        // EPI_ACC_F32: row block i's previous values in one batch of loads, then the stores
+        // (one wait per row block rather than per value, as for the pre-activation above).
+        float old[EPI == EPI_ACC_F32 ? NJ : 1][16];
+        if constexpr (EPI == EPI_ACC_F32) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int64_t row = row0 + 32 * i + 8 * (r >> 2) + (r & 3), col = col0 + 32 * j;
+              old[j][r] = row < M && col < N ? ((const float*)g.C)[row * ldc + col] : 0.0f;
+            }
+          wait_vmcnt<0>();
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int64_t col = col0 + 32 * j;
           if constexpr (EPI == EPI_ACC_F32) {
-            // Read the 16 values of the block, then write them back with the product added.
-            float old[16];
+            // The block's previous values were read with the rest of row block i (below).
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int64_t row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
-              old[r] = row < M && col < N ? ((const float*)g.C)[row * ldc + col] : 0.0f;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int64_t row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
-              if (row < M && col < N) ((float*)g.C)[row * ldc + col] = old[r] + acc[i][j][r];
+              if (row < M && col < N) ((float*)g.C)[row * ldc + col] = old[j][r] + acc[i][j][r];
             }
           } else {
 #pragma unroll

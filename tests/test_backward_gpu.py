@@ -280,3 +280,48 @@ def test_full_mlp_backward(lib):
     Y_cols = O.gelu_tanh(U_cols)
     check("dW2 block sampled rows", host(sh.dB[r * fl:(r + 1) * fl])[cols],
           Y_cols.T @ dZv.astype(np.float64), "bf16")
+
+
+# ============================================================== K tails in the first stages
+@pytest.mark.parametrize("kp", [8, 40, 64, 72, 96, 120, 136, 200])
+def test_short_contraction_every_layout(lib, kp):
+    """Products whose contraction length kp ends inside the first stages, which are loaded
+    before the K loop starts: the input-gradient product (B read K-contiguous, with and
+    without the GeLU' epilogue), the weight-gradient product (A read M-contiguous) and the
+    forward column product (A K-contiguous) must all zero-fill past kp.  Regression test: a
+    clobbered condition code once disabled the bound for these stages, so the loads ran on
+    into the next row."""
+    tp, pl = lib
+    rng = _rng(900 + kp)
+    seq, kl, N = 40, 256, kp  # dY = dZ[seq, kp] . W_r^T[kp, kl]; the forward uses H = kp
+    dZ, W = rng.standard_normal((seq, N)), rng.standard_normal((kl, N)) / np.sqrt(N)
+    U, Y = 1.5 * rng.standard_normal((seq, kl)), rng.standard_normal((seq, kl))
+    dZd, Wd, Ud, Yd = (dev_values(v, "bf16") for v in (dZ, W, U, Y))
+    dZv, Wv, Uv, Yv = (host(t) for t in (dZd, Wd, Ud, Yd))
+    for act in (tp.TP_ACT_NONE, tp.TP_ACT_GELU_TANH):
+        dY = torch.empty(seq, kl, dtype=torch.bfloat16, device="cuda:0")
+        say(f"  short contraction kp={kp} act={act}: input gradient (B^T read K-contiguous)")
+        tp.tp_row_linear_backward(dZd, Wd, None, 0, Ud, kl, dY, kl, None, 0, seq, kl, N, 0, 1, act,
+                                  0, tp.TP_BF16)
+        _sync()
+        rdY, _ = O.row_linear_backward(dZv, Yv, Wv, 0, 1, Uv,
+                                       "gelu_tanh" if act == tp.TP_ACT_GELU_TANH else "none")
+        check(f"dY kp={kp} act={act}", dY, rdY, "bf16")
+    # weight gradient with a short sequence: dW[kl, N] = Y[kp, kl]^T . dZ[kp, N]
+    Ys, dZs = rng.standard_normal((kp, kl)), rng.standard_normal((kp, 264))
+    Ysd, dZsd = dev_values(Ys, "bf16"), dev_values(dZs, "bf16")
+    dW = torch.empty(kl, 264, dtype=torch.float32, device="cuda:0")
+    say(f"  short contraction kp={kp}: weight gradient (A^T read M-contiguous)")
+    tp.tp_row_linear_backward(dZsd, dev_values(rng.standard_normal((kl, 264)), "bf16"), Ysd, kl,
+                              None, 0, None, 0, dW, 264, kp, kl, 264, 0, 1, tp.TP_ACT_NONE, 0,
+                              tp.TP_BF16)
+    _sync()
+    check(f"dW kp={kp}", dW, host(Ysd).T @ host(dZsd), "f32")
+    # forward column product with H = kp
+    X = dev_values(rng.standard_normal((seq, kp)), "bf16")
+    Wc = dev_values(rng.standard_normal((kp, 272)) / np.sqrt(kp), "bf16")
+    Yc = torch.empty(seq, 272, dtype=torch.bfloat16, device="cuda:0")
+    say(f"  short contraction kp={kp}: forward column product")
+    tp.tp_col_linear_gelu(X, Wc, Yc, 272, seq, kp, 272, 0, 1, tp.TP_ACT_GELU_TANH, tp.TP_BF16)
+    _sync()
+    check(f"Y kp={kp}", Yc, O.col_linear(host(X), host(Wc), 0, 1, "gelu_tanh"), "bf16")
