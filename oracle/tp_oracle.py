@@ -174,6 +174,19 @@ def reduce_partials(parts: Sequence[np.ndarray]) -> np.ndarray:
     return acc
 
 
+def row_linear_fold(Zsum, X, W, rank: int, world: int, accumulate: bool) -> np.ndarray:
+    """The reduce folded into the row-parallel product: rank r's partial is added to the
+    running sum Zsum as it is produced (accumulate), or starts it (rank 0, not accumulate),
+    instead of being kept for a separate reduce.  This is the fusion of the all-reduce with
+    its producer that [pwwt] section 2.3 (figure 5, fusing the all-reduce with the residual
+    add) and section 5.3 (fusion as the first saving) describe.  Folding ranks 0..P-1 in
+    ascending order performs the same additions as reduce_partials."""
+    part = row_linear_partial(X, W, rank, world)
+    if not accumulate:
+        return part
+    return _f64(Zsum) + part
+
+
 # ----------------------------------------------------------------------------- backward
 # The pages say that the backward pass of the split linears has its own communication
 # pattern and that each rank computes only the gradient of its own block of W, a gradient as
@@ -407,6 +420,17 @@ def attn_head_shard(Xn, Wqkv, Wo, n_heads: int, head_dim: int, rank: int, world:
     A = attention_heads(Xn, Wqkv, n_heads, head_dim, rank, world, batch, seq, causal, rows)
     h0, h1 = head_range(n_heads, world, rank)
     return matmul(A, Wo[h0 * head_dim: h1 * head_dim, :])
+
+
+def attn_head_shard_fold(Zsum, Xn, Wqkv, Wo, n_heads: int, head_dim: int, rank: int,
+                         world: int, batch: int, seq: int, causal: bool = True,
+                         accumulate: bool = True) -> np.ndarray:
+    """attn_head_shard with its output projection folded into the running sum Zsum, as
+    row_linear_fold does for the row-parallel linear ([pwwt] sections 2.3 and 5.3)."""
+    part = attn_head_shard(Xn, Wqkv, Wo, n_heads, head_dim, rank, world, batch, seq, causal)
+    if not accumulate:
+        return part
+    return _f64(Zsum) + part
 
 
 # ----------------------------------------------------------------------------- MLP, block

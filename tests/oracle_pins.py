@@ -129,6 +129,24 @@ def pin_row_partials_integer_exact():
         assert np.array_equal(O.reduce_partials(parts[::-1]), ref)
 
 
+def pin_row_fold_integer_exact():
+    """Folding the ranks' partials into one running sum, in ascending rank order, reaches the
+    un-split product exactly on integer inputs, and every intermediate running sum is the
+    brute-force product over the ranks folded so far.  Rank 0 (no accumulate) ignores
+    whatever the running sum held."""
+    rng = _rng(31)
+    X = _ints(rng, (6, 48), -2, 2)
+    W = _ints(rng, (48, 10), -3, 3)
+    for world in (1, 2, 3, 4, 8):
+        c = 48 // world
+        Z = np.full((6, 10), 1e6)
+        for r in range(world):
+            Z = O.row_linear_fold(Z, X, W, r, world, accumulate=r > 0)
+            assert np.array_equal(Z, brute_matmul(X[:, :(r + 1) * c], W[:(r + 1) * c])), \
+                f"running sum after rank {r} of {world}"
+        assert np.array_equal(Z, brute_matmul(X, W))
+
+
 def pin_row_partials_float():
     rng = _rng(14)
     X = rng.standard_normal((4, 6))
@@ -397,6 +415,21 @@ def pin_attention_head_split_equals_mha():
             parts = [O.attn_head_shard(Xn, Wqkv, Wo, nh, d, r, world, batch, seq, causal)
                      for r in range(world)]
             _close(O.reduce_partials(parts), ref, 1e-12, f"head split world={world}")
+
+
+def pin_attention_fold_equals_mha():
+    """The attention shards folded into one running sum in ascending rank order equal
+    torch's un-split multi-head attention, for every world size."""
+    batch, seq, nh, d = 2, 7, 4, 4
+    H = nh * d
+    Xn, Wqkv, Wo = _attn_inputs(32, batch, seq, H)
+    ref = _torch_mha(Xn, Wqkv, Wo, nh, batch, seq, True)
+    for world in (1, 2, 4):
+        Z = np.full((batch * seq, H), -3e5)
+        for r in range(world):
+            Z = O.attn_head_shard_fold(Z, Xn, Wqkv, Wo, nh, d, r, world, batch, seq, True,
+                                       accumulate=r > 0)
+        _close(Z, ref, 1e-12, f"folded heads world={world}")
 
 
 def pin_attention_rows_subset():

@@ -191,6 +191,18 @@ def _col_bwd_wgrad_uses_x_block(dU, X, W, rank, world):
     return dXp, X[:, :n].T @ np.asarray(dU, np.float64) if X.shape[1] >= n else X.T @ dU
 
 
+def _fold_ignores_running_sum(Zsum, X, W, rank, world, accumulate):
+    return _orig["row_linear_fold"](Zsum, X, W, rank, world, False)
+
+
+def _fold_always_accumulates(Zsum, X, W, rank, world, accumulate):
+    return _orig["row_linear_fold"](Zsum, X, W, rank, world, True)
+
+
+def _attn_fold_ignores_running_sum(Zsum, *args, accumulate=True, **kw):
+    return _orig["attn_head_shard_fold"](Zsum, *args, accumulate=False, **kw)
+
+
 MUTATIONS = {
     "shard_off_by_one": ("shard_range", _shard_off_by_one),
     "shard_reversed_ranks": ("shard_range", _shard_reversed),
@@ -224,6 +236,9 @@ MUTATIONS = {
     "row_bwd_weight_grad_transposed": ("row_linear_backward", _row_bwd_wgrad_transposed),
     "col_bwd_rank0_weight_block": ("col_linear_backward", _col_bwd_rank0_block),
     "col_bwd_weight_grad_x_block": ("col_linear_backward", _col_bwd_wgrad_uses_x_block),
+    "fold_ignores_running_sum": ("row_linear_fold", _fold_ignores_running_sum),
+    "fold_accumulates_on_rank0": ("row_linear_fold", _fold_always_accumulates),
+    "attn_fold_ignores_running_sum": ("attn_head_shard_fold", _attn_fold_ignores_running_sum),
 }
 
 
