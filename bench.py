@@ -20,7 +20,9 @@ sample of the same workload on this host.  After the timed steps, the sequence-p
 form of the epilogue (each rank's reduce-scatter of its 1024 rows) and the backward pass of
 the MLP pair (the four gradient products of every rank and the reduce of the input-gradient
 partials; --no-backward skips it) are timed on their own and reported beside the step,
-outside `value`.
+outside `value`, and so is the same step with each epilogue's reduce folded into the
+row-parallel products (one fp32 running sum instead of 8 stacked partials; --no-fold skips
+it).
 """
 from __future__ import annotations
 
@@ -162,6 +164,77 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
     return out
 
 
+def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
+    """The same block step with the reduce folded into the row-parallel products (each rank's
+    output projection and MLP row GEMM add their partial to one fp32 running sum in ascending
+    rank order; the epilogues then read one partial instead of 8).  Same weights and inputs as
+    the timed step; the outputs are bit-identical to it."""
+    import torch
+    from megatron_tensor_transformer_linear_amd import pipeline as pl
+    from workloads.configs import rank_flops, reduce_bytes
+
+    fb = pl.BlockShard(blk.X, blk.Wqkv, blk.Wo, blk.W1, blk.W2, blk.g1, blk.b1, blk.g2, blk.b2,
+                       cfg.world, cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, True, cfg.eps,
+                       fold=True)
+    keys = ("pre_ln", "attn", "reduce1", "mlp_col", "mlp_row", "reduce2")
+    ev = {k: [] for k in keys}
+
+    def timed(key, fn, record):
+        if record:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            ev[key].append((s, e))
+        else:
+            fn()
+
+    def step(record):
+        timed("pre_ln", fb.pre_ln, record)
+        for r in range(cfg.world):
+            timed("attn", lambda r=r: fb.attn(r), record)
+        timed("reduce1", fb.reduce1, record)
+        for r in range(cfg.world):
+            timed("mlp_col", lambda r=r: fb.mlp_col(r), record)
+            timed("mlp_row", lambda r=r: fb.mlp_row(r), record)
+        timed("reduce2", fb.reduce2, record)
+
+    step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fl = rank_flops(cfg)
+    step_flops = cfg.world * sum(fl.values())
+    T, H = cfg.tokens, cfg.hidden
+    r1 = reduce_bytes(T, H, 1, "bf16", residual=True, h_out=True, y_out=True)
+    r2 = reduce_bytes(T, H, 1, "bf16", residual=True, h_out=True, y_out=False)
+
+    def avg_ms(key):
+        return float(np.mean([s.elapsed_time(e) for s, e in ev[key]]))
+
+    out = {
+        "what": ("the block step with each epilogue's reduce folded into the row-parallel "
+                 "products' epilogues (one fp32 running sum, ranks added in ascending order); "
+                 "bit-identical outputs"),
+        "steps": steps,
+        "ms_per_step": round(elapsed / steps * 1e3, 3),
+        "tflops": round(step_flops * steps / elapsed / 1e12, 2),
+        "attn_avg_ms": round(avg_ms("attn"), 4),
+        "mlp_row_avg_ms": round(avg_ms("mlp_row"), 4),
+        "mlp_row_tflops": round(fl["mlp_row"] / avg_ms("mlp_row") / 1e9, 1),
+        "reduce1_ms": round(avg_ms("reduce1"), 4),
+        "reduce1_gbs": round(r1 / avg_ms("reduce1") / 1e6, 1),
+        "reduce2_ms": round(avg_ms("reduce2"), 4),
+        "reduce2_gbs": round(r2 / avg_ms("reduce2") / 1e6, 1),
+    }
+    del fb
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +243,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement of the MLP pair")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="skip the measurement of the step with folded reduces")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain copy kernel over MIB mebibytes (reads and writes "
                          "MIB each), the known-size reference for HBM byte counters")
@@ -336,6 +411,9 @@ def main() -> int:
     }
     if not args.no_backward:
         result["mlp_backward"] = mlp_backward_leg(cfg, t, blk, stream)
+    if not args.no_fold:
+        log("timing the block step with folded reduces")
+        result["folded_step"] = folded_block_leg(cfg, blk, stream, max(1, min(args.steps, 5)))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(cfg, t, np.hstack(

@@ -5,7 +5,8 @@
  * all-gather between GPUs, the caller concatenates the ranks' outputs in one HBM buffer
  * (by pointing each rank's output at its column block); where it places an all-reduce,
  * the ranks' fp32 partials are stacked in HBM and summed by
- * tp_partial_reduce_residual_ln, fused with the residual add and LayerNorm.
+ * tp_partial_reduce_residual_ln, fused with the residual add and LayerNorm, or summed in
+ * place by the producing product's epilogue (the *_fold calls).
  *
  * Sources (web pages on tensor parallelism):
  *   typc.net "张量并行：千亿大模型突破单卡显存限制的底层技术", sections 2.1, 2.2, 3;
@@ -98,6 +99,25 @@ int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpar
                           int64_t seq, int64_t K, int64_t N, int rank, int world,
                           int dtype, void* stream);
 
+/* Row-parallel linear with the reduce folded into the product's epilogue (pwwt.cn section
+ * 2.3: fusing the all-reduce with the residual add; section 5.3: fusion as the first way to
+ * save exchange).  The ranks' partials are summed in place as they are produced instead of
+ * being stacked and reduced afterwards:
+ *
+ *   accumulate == 0:  Zsum[t, n]  = sum_{k < K/world} X[t, k] * W[rank*K/world + k, n]
+ *   accumulate != 0:  Zsum[t, n] += sum_{k < K/world} X[t, k] * W[rank*K/world + k, n]
+ *
+ * Arguments, shard addressing and errors are those of tp_row_linear_partial, with Zsum
+ * [seq, N] dense fp32 in place of Zpart; Zsum must not overlap X or W.  Calling rank 0 with
+ * accumulate == 0 and then ranks 1..world-1 with accumulate != 0, in that order on one stream,
+ * leaves Zsum = ((Z_0 + Z_1) + ...) + Z_{world-1} in fp32, the same additions in the same
+ * order as tp_partial_reduce_residual_ln applies to the stacked partials.  Passing Zsum to
+ * that call with n_parts = 1 therefore gives bit-identical h and y, while the reduce reads
+ * one fp32 [seq, N] block instead of world of them and the stacked buffer is not needed. */
+int tp_row_linear_fold(const void* X, int64_t ldx, const void* W, float* Zsum,
+                       int64_t seq, int64_t K, int64_t N, int rank, int world,
+                       int accumulate, int dtype, void* stream);
+
 /* Column-parallel linear + GeLU that also keeps the pre-activation for the backward pass:
  * exactly tp_col_linear_gelu with act = TP_ACT_GELU_TANH, plus
  *
@@ -187,6 +207,16 @@ int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* 
                        int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
                        int rank, int world, int causal, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention-head shard with the reduce folded into the output projection's epilogue, as
+ * tp_row_linear_fold does for the row-parallel linear: the rank's A_r . Wo[rank rows, :] is
+ * written to Zsum [batch*seq, H] fp32 when accumulate == 0 and added to it otherwise.  All
+ * other arguments, the workspace contents and the errors are those of tp_attn_head_shard;
+ * Zsum must not overlap Xn, Wqkv, Wo or the workspace. */
+int tp_attn_head_shard_fold(const void* Xn, const void* Wqkv, const void* Wo, float* Zsum,
+                            int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                            int rank, int world, int causal, int accumulate, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* The all-reduce replacement, fused with the residual add and LayerNorm (pwwt.cn section
  * 2.3: the single all-reduce sits just before the residual add, and fusing it with the

@@ -735,7 +735,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
 template <int LAY, int EPI>
 constexpr bool layout_has_epilogue() {
   if (LAY == LAY_NN) return EPI == EPI_STORE || EPI == EPI_GELU_TANH || EPI == EPI_PARTIAL_F32 ||
-                            EPI == EPI_GELU_SAVE;
+                            EPI == EPI_GELU_SAVE || EPI == EPI_ACC_F32;
   if (LAY == LAY_NT) return EPI == EPI_STORE || EPI == EPI_GELU_BWD || EPI == EPI_PARTIAL_F32;
   if (LAY == LAY_TN) return EPI == EPI_PARTIAL_F32 || EPI == EPI_ACC_F32;
   return false;

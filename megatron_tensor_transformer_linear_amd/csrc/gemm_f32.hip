@@ -80,7 +80,9 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmDesc g) {
         if (row >= M) continue;
         float v = acc[i][j][r];
         if (EPI == EPI_GELU_TANH) v = gelu_tanh_f32(v);
-        ((float*)g.C)[row * g.ldc + col] = v;
+        float* c = (float*)g.C + row * g.ldc + col;
+        if (EPI == EPI_ACC_F32) v = *c + v;
+        *c = v;
       }
     }
 }
@@ -96,6 +98,7 @@ hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t stream) {
     case EPI_STORE:
     case EPI_PARTIAL_F32: hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, grid, block, 0, stream, g); break;
     case EPI_GELU_TANH: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU_TANH>, grid, block, 0, stream, g); break;
+    case EPI_ACC_F32: hipLaunchKernelGGL(gemm_f32_kernel<EPI_ACC_F32>, grid, block, 0, stream, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

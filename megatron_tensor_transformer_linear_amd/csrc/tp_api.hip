@@ -47,6 +47,109 @@ int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
   return TP_OK;
 }
 
+// Rank `rank`'s row-parallel product into the fp32 Z [seq, N]: written (EPI_PARTIAL_F32) or
+// added to what Z holds (EPI_ACC_F32).
+int row_linear(const void* X, int64_t ldx, const void* W, float* Z, int64_t seq, int64_t K,
+               int64_t N, int rank, int world, int epi, int dtype, void* stream) {
+  if (!X || !W || !Z) return TP_ERR_NULL;
+  if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  if (seq <= 0 || K <= 0 || N <= 0) return TP_ERR_SHAPE;
+  if (K % world) return TP_ERR_DIVISIBLE;
+  const int64_t kl = K / world;
+  if (ldx < kl) return TP_ERR_SHAPE;
+  if (ldx > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Z)) return TP_ERR_ALIGN;
+  if (!mult8(ldx) || !mult8(kl) || !mult8(N)) return TP_ERR_ALIGN;
+
+  const size_t es = dtype == TP_BF16 ? 2 : 4;
+  GemmDesc g;
+  g.A = X;                                             // the rank's input shard [seq, K/world]
+  g.lda = ldx;
+  g.B = (const char*)W + (size_t)rank * kl * N * es;   // row block `rank` of W[K, N]
+  g.ldb = N;
+  g.b_blk = N;
+  g.b_blk_stride = 0;
+  g.n_off = 0;
+  g.C = Z;
+  g.ldc = N;
+  g.M = seq;
+  g.N = N;
+  g.K = kl;
+  g.epi = epi;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  return launched(dtype == TP_BF16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s));
+}
+
+// Rank `rank`'s attention head shard; its output projection writes (EPI_PARTIAL_F32) or adds
+// to (EPI_ACC_F32) the fp32 Z [batch*seq, H].
+int attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
+                    int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim, int rank,
+                    int world, int causal, int epi, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (!Xn || !Wqkv || !Wo || !Zpart) return TP_ERR_NULL;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  AttnSizes s;
+  if (int st = attn_sizes(batch, seq, H, n_heads, head_dim, world, &s)) return st;
+  if (!workspace || workspace_bytes < (size_t)s.total) return TP_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return TP_ERR_ALIGN;
+  if (!aligned16(Xn) || !aligned16(Wqkv) || !aligned16(Wo) || !aligned16(Zpart))
+    return TP_ERR_ALIGN;
+
+  bf16_t* ws_qkv = (bf16_t*)workspace;
+  bf16_t* ws_a = (bf16_t*)((char*)workspace + s.qkv_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+
+  // Column-parallel QKV: logical column n of the rank's [Q_r | K_r | V_r] is physical column
+  // (n / nb) * H + rank * nb + n % nb of [Wq | Wk | Wv].
+  GemmDesc q;
+  q.A = Xn;
+  q.lda = H;
+  q.B = (const bf16_t*)Wqkv + (size_t)rank * s.nb;
+  q.ldb = 3 * H;
+  q.b_blk = s.nb;
+  q.b_blk_stride = H;
+  q.n_off = 0;
+  q.C = ws_qkv;
+  q.ldc = 3 * s.nb;
+  q.M = s.T;
+  q.N = 3 * s.nb;
+  q.K = H;
+  q.epi = EPI_STORE;
+  if (launch_gemm_bf16(q, st) != hipSuccess) return TP_ERR_LAUNCH;
+
+  AttnDesc a;
+  a.qkv = ws_qkv;
+  a.out = ws_a;
+  a.batch = batch;
+  a.seq = seq;
+  a.hl = (int)s.hl;
+  a.d = head_dim;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  if (launch_attention(a, st) != hipSuccess) return TP_ERR_LAUNCH;
+
+  // Row-parallel output projection over the rank's rows of Wo.
+  GemmDesc o;
+  o.A = ws_a;
+  o.lda = s.nb;
+  o.B = (const bf16_t*)Wo + (size_t)rank * s.nb * H;
+  o.ldb = H;
+  o.b_blk = H;
+  o.b_blk_stride = 0;
+  o.n_off = 0;
+  o.C = Zpart;
+  o.ldc = H;
+  o.M = s.T;
+  o.N = H;
+  o.K = s.nb;
+  o.epi = epi;
+  return launched(launch_gemm_bf16(o, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,35 +206,14 @@ int tp_col_linear_gelu(const void* X, const void* W, void* Y, int64_t ldy, int64
 
 int tp_row_linear_partial(const void* X, int64_t ldx, const void* W, float* Zpart, int64_t seq,
                           int64_t K, int64_t N, int rank, int world, int dtype, void* stream) {
-  if (!X || !W || !Zpart) return TP_ERR_NULL;
-  if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
-  if (int st = check_rank(rank, world)) return st;
-  if (seq <= 0 || K <= 0 || N <= 0) return TP_ERR_SHAPE;
-  if (K % world) return TP_ERR_DIVISIBLE;
-  const int64_t kl = K / world;
-  if (ldx < kl) return TP_ERR_SHAPE;
-  if (ldx > MAX_LD_ACT || N > MAX_LD_WEIGHT) return TP_ERR_SHAPE;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(Zpart)) return TP_ERR_ALIGN;
-  if (!mult8(ldx) || !mult8(kl) || !mult8(N)) return TP_ERR_ALIGN;
+  return row_linear(X, ldx, W, Zpart, seq, K, N, rank, world, EPI_PARTIAL_F32, dtype, stream);
+}
 
-  const size_t es = dtype == TP_BF16 ? 2 : 4;
-  GemmDesc g;
-  g.A = X;                                             // the rank's input shard [seq, K/world]
-  g.lda = ldx;
-  g.B = (const char*)W + (size_t)rank * kl * N * es;   // row block `rank` of W[K, N]
-  g.ldb = N;
-  g.b_blk = N;
-  g.b_blk_stride = 0;
-  g.n_off = 0;
-  g.C = Zpart;
-  g.ldc = N;
-  g.M = seq;
-  g.N = N;
-  g.K = kl;
-  g.epi = EPI_PARTIAL_F32;
-  (void)hipGetLastError();
-  hipStream_t s = (hipStream_t)stream;
-  return launched(dtype == TP_BF16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s));
+int tp_row_linear_fold(const void* X, int64_t ldx, const void* W, float* Zsum, int64_t seq,
+                       int64_t K, int64_t N, int rank, int world, int accumulate, int dtype,
+                       void* stream) {
+  return row_linear(X, ldx, W, Zsum, seq, K, N, rank, world,
+                    accumulate ? EPI_ACC_F32 : EPI_PARTIAL_F32, dtype, stream);
 }
 
 int tp_col_linear_gelu_save(const void* X, const void* W, void* Y, int64_t ldy, void* U,
@@ -310,66 +392,17 @@ int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* 
                        int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
                        int rank, int world, int causal, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  if (!Xn || !Wqkv || !Wo || !Zpart) return TP_ERR_NULL;
-  if (dtype != TP_BF16) return TP_ERR_DTYPE;
-  if (int st = check_rank(rank, world)) return st;
-  AttnSizes s;
-  if (int st = attn_sizes(batch, seq, H, n_heads, head_dim, world, &s)) return st;
-  if (!workspace || workspace_bytes < (size_t)s.total) return TP_ERR_WORKSPACE;
-  if (((uintptr_t)workspace & 255u) != 0) return TP_ERR_ALIGN;
-  if (!aligned16(Xn) || !aligned16(Wqkv) || !aligned16(Wo) || !aligned16(Zpart))
-    return TP_ERR_ALIGN;
+  return attn_head_shard(Xn, Wqkv, Wo, Zpart, batch, seq, H, n_heads, head_dim, rank, world,
+                         causal, EPI_PARTIAL_F32, dtype, workspace, workspace_bytes, stream);
+}
 
-  bf16_t* ws_qkv = (bf16_t*)workspace;
-  bf16_t* ws_a = (bf16_t*)((char*)workspace + s.qkv_bytes);
-  hipStream_t st = (hipStream_t)stream;
-  (void)hipGetLastError();
-
-  // Column-parallel QKV: logical column n of the rank's [Q_r | K_r | V_r] is physical column
-  // (n / nb) * H + rank * nb + n % nb of [Wq | Wk | Wv].
-  GemmDesc q;
-  q.A = Xn;
-  q.lda = H;
-  q.B = (const bf16_t*)Wqkv + (size_t)rank * s.nb;
-  q.ldb = 3 * H;
-  q.b_blk = s.nb;
-  q.b_blk_stride = H;
-  q.n_off = 0;
-  q.C = ws_qkv;
-  q.ldc = 3 * s.nb;
-  q.M = s.T;
-  q.N = 3 * s.nb;
-  q.K = H;
-  q.epi = EPI_STORE;
-  if (launch_gemm_bf16(q, st) != hipSuccess) return TP_ERR_LAUNCH;
-
-  AttnDesc a;
-  a.qkv = ws_qkv;
-  a.out = ws_a;
-  a.batch = batch;
-  a.seq = seq;
-  a.hl = (int)s.hl;
-  a.d = head_dim;
-  a.causal = causal ? 1 : 0;
-  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
-  if (launch_attention(a, st) != hipSuccess) return TP_ERR_LAUNCH;
-
-  // Row-parallel output projection over the rank's rows of Wo.
-  GemmDesc o;
-  o.A = ws_a;
-  o.lda = s.nb;
-  o.B = (const bf16_t*)Wo + (size_t)rank * s.nb * H;
-  o.ldb = H;
-  o.b_blk = H;
-  o.b_blk_stride = 0;
-  o.n_off = 0;
-  o.C = Zpart;
-  o.ldc = H;
-  o.M = s.T;
-  o.N = H;
-  o.K = s.nb;
-  o.epi = EPI_PARTIAL_F32;
-  return launched(launch_gemm_bf16(o, st));
+int tp_attn_head_shard_fold(const void* Xn, const void* Wqkv, const void* Wo, float* Zsum,
+                            int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                            int rank, int world, int causal, int accumulate, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_head_shard(Xn, Wqkv, Wo, Zsum, batch, seq, H, n_heads, head_dim, rank, world,
+                         causal, accumulate ? EPI_ACC_F32 : EPI_PARTIAL_F32, dtype, workspace,
+                         workspace_bytes, stream);
 }
 
 int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_stride,

@@ -47,10 +47,14 @@ class MLPShard:
     """Column-parallel A (GeLU) then row-parallel B, P ranks, then the fused reduce.
 
     residual_ln=True: h = X + sum_r Z_r and y = LN(h) (io dtype).  Otherwise the partials
-    are only summed, into Z (fp32)."""
+    are only summed, into Z (fp32).
+
+    fold=True folds the reduce into the row-parallel products: rank 0 writes one fp32 running
+    sum and ranks 1..P-1 add to it in ascending order, so the reduce reads one partial instead
+    of P (pwwt.cn sections 2.3, 5.3); the additions are the stacked reduce's, in its order."""
 
     def __init__(self, X, A, B, world: int, dtype: str, gamma=None, beta=None,
-                 eps: float = 1e-5, residual_ln: bool = True, stream=None):
+                 eps: float = 1e-5, residual_ln: bool = True, stream=None, fold: bool = False):
         self.X, self.A, self.B = X, A, B
         self.T, self.H = X.shape
         self.F = A.shape[1]
@@ -59,9 +63,12 @@ class MLPShard:
         self.gamma, self.beta, self.eps = gamma, beta, eps
         self.residual_ln = residual_ln
         self.stream = stream
+        self.fold = fold
         dev = X.device
         self.Yfull = torch.empty(self.T, self.F, dtype=torch_dtype(dtype), device=dev)
-        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
+        self.n_parts = 1 if fold else world
+        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
         if residual_ln:
             self.h = torch.empty(self.T, self.H, dtype=torch_dtype(dtype), device=dev)
             self.y = torch.empty_like(self.h)
@@ -75,18 +82,22 @@ class MLPShard:
 
     def row(self, r: int):
         fl = self.F // self.P
+        if self.fold:
+            tp.tp_row_linear_fold(self.Yfull[:, r * fl:], self.F, self.B, self.parts[0], self.T,
+                                  self.F, self.H, r, self.P, int(r > 0), self.dt, self.stream)
+            return
         tp.tp_row_linear_partial(self.Yfull[:, r * fl:], self.F, self.B, self.parts[r], self.T,
                                  self.F, self.H, r, self.P, self.dt, self.stream)
 
     def reduce(self):
         n = self.T * self.H
         if self.residual_ln:
-            tp.tp_partial_reduce_residual_ln(self.parts, self.P, n, self.X, self.gamma, self.beta,
-                                             self.eps, self.h, self.y, self.T, self.H, self.dt,
-                                             self.stream)
+            tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, n, self.X, self.gamma,
+                                             self.beta, self.eps, self.h, self.y, self.T, self.H,
+                                             self.dt, self.stream)
         else:
-            tp.tp_partial_reduce_residual_ln(self.parts, self.P, n, None, None, None, 0.0, self.Z,
-                                             None, self.T, self.H, tp.TP_F32, self.stream)
+            tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, n, None, None, None, 0.0,
+                                             self.Z, None, self.T, self.H, tp.TP_F32, self.stream)
 
     def step(self):
         for r in range(self.P):
@@ -171,9 +182,14 @@ class MLPTrainShard:
 
 class LinearShard:
     """One linear X[T,H].W[H,N]: the column block of chosen ranks, and the row split of
-    every rank with the fp32 partial sum Z."""
+    every rank with the fp32 partial sum Z.
 
-    def __init__(self, X, W, world: int, dtype: str, col_ranks=(0,), stream=None):
+    fold=True folds the reduce into the row-parallel products: rank 0 writes one fp32 running
+    sum and ranks 1..P-1 add to it in ascending order, so the reduce reads one partial instead
+    of P (pwwt.cn sections 2.3, 5.3); the additions are the stacked reduce's, in its order."""
+
+    def __init__(self, X, W, world: int, dtype: str, col_ranks=(0,), stream=None,
+                 fold: bool = False):
         self.X, self.W = X, W
         self.T, self.H = X.shape
         self.N = W.shape[1]
@@ -185,7 +201,9 @@ class LinearShard:
         nl = self.N // world
         self.Ycol = {r: torch.empty(self.T, nl, dtype=torch_dtype(dtype), device=dev)
                      for r in self.col_ranks}
-        self.parts = torch.empty(world, self.T, self.N, dtype=torch.float32, device=dev)
+        self.fold = fold
+        self.n_parts = 1 if fold else world
+        self.parts = torch.empty(self.n_parts, self.T, self.N, dtype=torch.float32, device=dev)
         self.Z = torch.empty(self.T, self.N, dtype=torch.float32, device=dev)
 
     def column(self, r: int, act: int = tp.TP_ACT_NONE):
@@ -195,12 +213,17 @@ class LinearShard:
 
     def row(self, r: int):
         kl = self.H // self.P
+        if self.fold:
+            tp.tp_row_linear_fold(self.X[:, r * kl:], self.H, self.W, self.parts[0], self.T,
+                                  self.H, self.N, r, self.P, int(r > 0), self.dt, self.stream)
+            return
         tp.tp_row_linear_partial(self.X[:, r * kl:], self.H, self.W, self.parts[r], self.T,
                                  self.H, self.N, r, self.P, self.dt, self.stream)
 
     def reduce(self):
-        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.N, None, None, None,
-                                         0.0, self.Z, None, self.T, self.N, tp.TP_F32, self.stream)
+        tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, self.T * self.N, None, None,
+                                         None, 0.0, self.Z, None, self.T, self.N, tp.TP_F32,
+                                         self.stream)
 
     def step(self):
         for r in self.col_ranks:
@@ -211,22 +234,29 @@ class LinearShard:
 
 
 class AttnShard:
-    """The attention-head shard of every rank, and the fp32 sum of their partials."""
+    """The attention-head shard of every rank, and the fp32 sum of their partials.
+
+    fold=True folds the reduce into the row-parallel products: rank 0 writes one fp32 running
+    sum and ranks 1..P-1 add to it in ascending order, so the reduce reads one partial instead
+    of P (pwwt.cn sections 2.3, 5.3); the additions are the stacked reduce's, in its order."""
 
     def __init__(self, Xn, Wqkv, Wo, world: int, batch: int, seq: int, n_heads: int,
-                 head_dim: int, causal: bool = True, stream=None):
+                 head_dim: int, causal: bool = True, stream=None, fold: bool = False):
         self.Xn, self.Wqkv, self.Wo = Xn, Wqkv, Wo
         self.T, self.H = Xn.shape
         self.P, self.batch, self.seq = world, batch, seq
         self.nh, self.d, self.causal = n_heads, head_dim, causal
         self.stream = stream
+        self.fold = fold
         dev = Xn.device
         self.ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, self.H, n_heads, head_dim, world,
                                                    tp.TP_BF16)
         if self.ws_bytes == 0:
             raise ValueError("invalid attention sizes")
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
-        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
+        self.n_parts = 1 if fold else world
+        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
         self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
 
     def workspace_views(self):
@@ -237,13 +267,21 @@ class AttnShard:
         return flat[:n_qkv].view(self.T, 3 * nb), flat[n_qkv:n_qkv + self.T * nb].view(self.T, nb)
 
     def rank(self, r: int, out: Optional[torch.Tensor] = None):
+        if self.fold:
+            tp.tp_attn_head_shard_fold(self.Xn, self.Wqkv, self.Wo,
+                                       self.parts[0] if out is None else out, self.batch,
+                                       self.seq, self.H, self.nh, self.d, r, self.P,
+                                       int(self.causal), int(r > 0), tp.TP_BF16, self.ws,
+                                       self.ws_bytes, self.stream)
+            return
         tp.tp_attn_head_shard(self.Xn, self.Wqkv, self.Wo, self.parts[r] if out is None else out,
                               self.batch, self.seq, self.H, self.nh, self.d, r, self.P,
                               int(self.causal), tp.TP_BF16, self.ws, self.ws_bytes, self.stream)
 
     def reduce(self):
-        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, None, None, None,
-                                         0.0, self.Z, None, self.T, self.H, tp.TP_F32, self.stream)
+        tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, self.T * self.H, None, None,
+                                         None, 0.0, self.Z, None, self.T, self.H, tp.TP_F32,
+                                         self.stream)
 
     def step(self):
         for r in range(self.P):
@@ -257,11 +295,17 @@ class BlockShard:
 
     sequence_parallel=True runs each epilogue as the ranks' reduce-scatters (rank r sums,
     adds the residual to and normalises rows [r T/P, (r+1) T/P)) writing into the full
-    buffers at their row offsets, which is the all-gather (pwwt.cn sections 5.1, 5.3)."""
+    buffers at their row offsets, which is the all-gather (pwwt.cn sections 5.1, 5.3).
+
+    fold=True folds the reduce into the row-parallel products: rank 0's output projection
+    writes one fp32 [T, H] running sum and ranks 1..P-1 add to it in ascending order, so each
+    epilogue reads one partial instead of P (pwwt.cn sections 2.3, 5.3).  The additions are
+    the stacked reduce's, in its order, so every output is bit-identical."""
 
     def __init__(self, X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, world: int,
                  batch: int, seq: int, n_heads: int, head_dim: int, causal: bool = True,
-                 eps: float = 1e-5, stream=None, sequence_parallel: bool = False):
+                 eps: float = 1e-5, stream=None, sequence_parallel: bool = False,
+                 fold: bool = False):
         self.X, self.Wqkv, self.Wo, self.W1, self.W2 = X, Wqkv, Wo, W1, W2
         self.g1, self.b1, self.g2, self.b2 = gamma1, beta1, gamma2, beta2
         self.T, self.H = X.shape
@@ -270,6 +314,7 @@ class BlockShard:
         self.nh, self.d, self.causal, self.eps = n_heads, head_dim, causal, eps
         self.stream = stream
         self.sequence_parallel = sequence_parallel
+        self.fold = fold
         if sequence_parallel and self.T % world:
             raise ValueError("sequence parallelism needs tokens divisible by the world size")
         dev = X.device
@@ -281,7 +326,9 @@ class BlockShard:
         # The hidden activation stays with its rank: Yr[r] = GeLU(hn . W1_r), dense
         # [T, F/P], is the row call's input shard (no gather between the two MLP GEMMs).
         self.Yr = torch.empty(world, self.T, self.F // world, dtype=bf, device=dev)
-        self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
+        # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
+        self.n_parts = 1 if fold else world
+        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
         self.ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, self.H, n_heads, head_dim, world,
                                                    tp.TP_BF16)
         if self.ws_bytes == 0:
@@ -293,6 +340,12 @@ class BlockShard:
                                          self.xn, self.T, self.H, tp.TP_BF16, self.stream)
 
     def attn(self, r: int):
+        if self.fold:
+            tp.tp_attn_head_shard_fold(self.xn, self.Wqkv, self.Wo, self.parts[0], self.batch,
+                                       self.seq, self.H, self.nh, self.d, r, self.P,
+                                       int(self.causal), int(r > 0), tp.TP_BF16, self.ws,
+                                       self.ws_bytes, self.stream)
+            return
         tp.tp_attn_head_shard(self.xn, self.Wqkv, self.Wo, self.parts[r], self.batch, self.seq,
                               self.H, self.nh, self.d, r, self.P, int(self.causal), tp.TP_BF16,
                               self.ws, self.ws_bytes, self.stream)
@@ -307,14 +360,14 @@ class BlockShard:
             for r in range(self.P):
                 self.reduce1_scatter(r)
             return
-        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.X, self.g2,
+        tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, self.T * self.H, self.X, self.g2,
                                          self.b2, self.eps, self.h, self.hn, self.T, self.H,
                                          tp.TP_BF16, self.stream)
 
     def reduce1_scatter(self, r: int):
         """Rank r's reduce-scatter + residual + LN2 into its rows of h and hn."""
         a, n = self._scatter_rows(r)
-        tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.P, self.T * self.H, self.X,
+        tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.n_parts, self.T * self.H, self.X,
                                                  self.g2, self.b2, self.eps, self.h[a:a + n],
                                                  self.hn[a:a + n], self.T, self.H, r, self.P,
                                                  tp.TP_BF16, self.stream)
@@ -326,6 +379,10 @@ class BlockShard:
 
     def mlp_row(self, r: int):
         fl = self.F // self.P
+        if self.fold:
+            tp.tp_row_linear_fold(self.Yr[r], fl, self.W2, self.parts[0], self.T, self.F, self.H,
+                                  r, self.P, int(r > 0), tp.TP_BF16, self.stream)
+            return
         tp.tp_row_linear_partial(self.Yr[r], fl, self.W2, self.parts[r], self.T, self.F, self.H,
                                  r, self.P, tp.TP_BF16, self.stream)
 
@@ -334,14 +391,14 @@ class BlockShard:
             for r in range(self.P):
                 self.reduce2_scatter(r)
             return
-        tp.tp_partial_reduce_residual_ln(self.parts, self.P, self.T * self.H, self.h, None, None,
-                                         0.0, self.out, None, self.T, self.H, tp.TP_BF16,
+        tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, self.T * self.H, self.h, None,
+                                         None, 0.0, self.out, None, self.T, self.H, tp.TP_BF16,
                                          self.stream)
 
     def reduce2_scatter(self, r: int):
         """Rank r's reduce-scatter + residual into its rows of out."""
         a, n = self._scatter_rows(r)
-        tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.P, self.T * self.H, self.h,
+        tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.n_parts, self.T * self.H, self.h,
                                                  None, None, 0.0, self.out[a:a + n], None,
                                                  self.T, self.H, r, self.P, tp.TP_BF16,
                                                  self.stream)

@@ -28,9 +28,10 @@ TP_BF16 = 1
 TP_ACT_NONE = 0
 TP_ACT_GELU_TANH = 1
 
-EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_col_linear_gelu_save",
-            "tp_row_linear_backward", "tp_col_linear_backward", "tp_attn_workspace_bytes",
-            "tp_attn_head_shard", "tp_partial_reduce_residual_ln",
+EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_row_linear_fold",
+            "tp_col_linear_gelu_save", "tp_row_linear_backward", "tp_col_linear_backward",
+            "tp_attn_workspace_bytes", "tp_attn_head_shard", "tp_attn_head_shard_fold",
+            "tp_partial_reduce_residual_ln",
             "tp_partial_reduce_scatter_residual_ln", "tp_status_string")
 
 if not os.path.exists(LIB_PATH):
@@ -44,6 +45,9 @@ lib.tp_col_linear_gelu.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, 
 lib.tp_col_linear_gelu.restype = _int
 lib.tp_row_linear_partial.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]
 lib.tp_row_linear_partial.restype = _int
+lib.tp_row_linear_fold.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
+                                   _vp]
+lib.tp_row_linear_fold.restype = _int
 lib.tp_col_linear_gelu_save.argtypes = [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int,
                                         _int, _int, _vp]
 lib.tp_col_linear_gelu_save.restype = _int
@@ -58,6 +62,9 @@ lib.tp_attn_workspace_bytes.restype = _sz
 lib.tp_attn_head_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
                                    _int, _int, _vp, _sz, _vp]
 lib.tp_attn_head_shard.restype = _int
+lib.tp_attn_head_shard_fold.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
+                                        _int, _int, _int, _int, _vp, _sz, _vp]
+lib.tp_attn_head_shard_fold.restype = _int
 lib.tp_partial_reduce_residual_ln.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp, _vp,
                                               _i64, _i64, _int, _vp]
 lib.tp_partial_reduce_residual_ln.restype = _int
@@ -113,6 +120,13 @@ def tp_row_linear_partial(X, ldx: int, W, Zpart, seq: int, K: int, N: int, rank:
                                             world, dtype, _stream(stream)), "tp_row_linear_partial")
 
 
+def tp_row_linear_fold(X, ldx: int, W, Zsum, seq: int, K: int, N: int, rank: int, world: int,
+                       accumulate: int, dtype: int, stream=None) -> int:
+    return _check(lib.tp_row_linear_fold(_ptr(X), ldx, _ptr(W), _ptr(Zsum), seq, K, N, rank, world,
+                                         int(accumulate), dtype, _stream(stream)),
+                  "tp_row_linear_fold")
+
+
 def tp_col_linear_gelu_save(X, W, Y, ldy: int, U, ldu: int, seq: int, H: int, N: int, rank: int,
                             world: int, dtype: int, stream=None) -> int:
     return _check(lib.tp_col_linear_gelu_save(_ptr(X), _ptr(W), _ptr(Y), ldy, _ptr(U), ldu, seq, H,
@@ -150,6 +164,16 @@ def tp_attn_head_shard(Xn, Wqkv, Wo, Zpart, batch: int, seq: int, H: int, n_head
                                          H, n_heads, head_dim, rank, world, int(causal), dtype,
                                          _ptr(workspace), workspace_bytes, _stream(stream)),
                   "tp_attn_head_shard")
+
+
+def tp_attn_head_shard_fold(Xn, Wqkv, Wo, Zsum, batch: int, seq: int, H: int, n_heads: int,
+                            head_dim: int, rank: int, world: int, causal: int, accumulate: int,
+                            dtype: int, workspace, workspace_bytes: int, stream=None) -> int:
+    return _check(lib.tp_attn_head_shard_fold(_ptr(Xn), _ptr(Wqkv), _ptr(Wo), _ptr(Zsum), batch,
+                                              seq, H, n_heads, head_dim, rank, world, int(causal),
+                                              int(accumulate), dtype, _ptr(workspace),
+                                              workspace_bytes, _stream(stream)),
+                  "tp_attn_head_shard_fold")
 
 
 def tp_partial_reduce_residual_ln(parts, n_parts: int, part_stride: int, residual, gamma, beta,

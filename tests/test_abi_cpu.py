@@ -87,6 +87,24 @@ def attn(tp, **kw):
                                      a["dtype"], a["ws"], a["wsb"], a["stream"])
 
 
+def rowf(tp, **kw):
+    a = dict(X=P, ldx=1024, W=P, Z=P, seq=64, K=1024, N=256, rank=1, world=2, acc=1,
+             dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_row_linear_fold(a["X"], a["ldx"], a["W"], a["Z"], a["seq"], a["K"], a["N"],
+                                     a["rank"], a["world"], a["acc"], a["dtype"], a["stream"])
+
+
+def attnf(tp, **kw):
+    a = dict(Xn=P, Wqkv=P, Wo=P, Z=P, batch=2, seq=64, H=1024, nh=8, d=128, rank=1, world=4,
+             causal=1, acc=1, dtype=tp.TP_BF16, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return tp.lib.tp_attn_head_shard_fold(a["Xn"], a["Wqkv"], a["Wo"], a["Z"], a["batch"],
+                                          a["seq"], a["H"], a["nh"], a["d"], a["rank"],
+                                          a["world"], a["causal"], a["acc"], a["dtype"], a["ws"],
+                                          a["wsb"], a["stream"])
+
+
 def red(tp, **kw):
     a = dict(parts=P, n=4, stride=64 * 256, res=P, g=P, b=P, eps=1e-5, h=P, y=P, rows=64, H=256,
              dtype=tp.TP_BF16, stream=None)
@@ -169,6 +187,20 @@ CASES = [
     ("row ldx % 8", row, dict(ldx=1028), "TP_ERR_ALIGN"),
     ("row ldx beyond 2^21", row, dict(ldx=(1 << 21) + 8), "TP_ERR_SHAPE"),
     ("row N beyond 2^23", row, dict(N=(1 << 23) + 8), "TP_ERR_SHAPE"),
+    # row-parallel linear folded into the running sum
+    ("fold null X", rowf, dict(X=None), "TP_ERR_NULL"),
+    ("fold null W", rowf, dict(W=None), "TP_ERR_NULL"),
+    ("fold null Z", rowf, dict(Z=None), "TP_ERR_NULL"),
+    ("fold bad dtype", rowf, dict(dtype=2), "TP_ERR_DTYPE"),
+    ("fold rank = world", rowf, dict(rank=2), "TP_ERR_RANK"),
+    ("fold world 0", rowf, dict(world=0, rank=0), "TP_ERR_RANK"),
+    ("fold seq 0", rowf, dict(seq=0), "TP_ERR_SHAPE"),
+    ("fold ldx < K/world", rowf, dict(ldx=504), "TP_ERR_SHAPE"),
+    ("fold K % world", rowf, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("fold misaligned Z", rowf, dict(Z=P + 4), "TP_ERR_ALIGN"),
+    ("fold N % 8", rowf, dict(N=252), "TP_ERR_ALIGN"),
+    ("fold ldx beyond 2^21", rowf, dict(ldx=(1 << 21) + 8), "TP_ERR_SHAPE"),
+    ("fold first rank null Z", rowf, dict(Z=None, acc=0, rank=0), "TP_ERR_NULL"),
     # attention-head shard
     ("attn null Wo", attn, dict(Wo=None), "TP_ERR_NULL"),
     ("attn f32", attn, dict(dtype=0), "TP_ERR_DTYPE"),
@@ -182,6 +214,15 @@ CASES = [
     ("attn small workspace", attn, dict(wsb=1000), "TP_ERR_WORKSPACE"),
     ("attn misaligned workspace", attn, dict(ws=P + 16), "TP_ERR_ALIGN"),
     ("attn misaligned Xn", attn, dict(Xn=P + 2), "TP_ERR_ALIGN"),
+    # attention-head shard folded into the running sum
+    ("attn fold null Z", attnf, dict(Z=None), "TP_ERR_NULL"),
+    ("attn fold null Xn", attnf, dict(Xn=None), "TP_ERR_NULL"),
+    ("attn fold f32", attnf, dict(dtype=0), "TP_ERR_DTYPE"),
+    ("attn fold rank = world", attnf, dict(rank=4), "TP_ERR_RANK"),
+    ("attn fold head_dim 64", attnf, dict(d=64, nh=16), "TP_ERR_SHAPE"),
+    ("attn fold heads % world", attnf, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("attn fold small workspace", attnf, dict(wsb=1000), "TP_ERR_WORKSPACE"),
+    ("attn fold misaligned Z", attnf, dict(Z=P + 8), "TP_ERR_ALIGN"),
     # reduce + residual + LN
     ("reduce bad dtype", red, dict(dtype=9), "TP_ERR_DTYPE"),
     ("reduce negative parts", red, dict(n=-1), "TP_ERR_SHAPE"),
