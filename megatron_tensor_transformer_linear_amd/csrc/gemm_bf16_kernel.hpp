@@ -251,6 +251,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   static_assert(BN == 256 || BN == 192 || BN == 128, "tile width");
   static_assert(BM == 256 || BM == 128, "tile height");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  // bf16 outputs leave through LDS (see the epilogue): each wave owns a 32 x WN block of
+  // its own, beside the stage ring (whose slots hold the next tile's stages by then).  Not
+  // with EPI_GELU_BWD: its pre-activation batch already fills the registers, and staging
+  // made the compiler spill.
+  constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU_TANH || EPI == EPI_GELU_SAVE) &&
+                          (WN == 128 || WN == 64);
+  constexpr int EPITCH = WN * 2;  // bytes per staged row
+  constexpr int ECH = WN / 8;     // 16-byte chunks per staged row
+  __shared__ __attribute__((aligned(16))) char epi_smem[STAGED ? 4 * 32 * EPITCH : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -650,38 +659,77 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         // without it the compiler waits for every earlier store before each use of a value.
         wait_vmcnt<0>();
       }
+      // Item (i, j, qq) of the lane: output row 32 i + lane % 32 (of the wave's block), columns
+      // 32 j + 8 qq + 4 (lane / 32) + 0..3, as 4 packed bf16; the pre-activation (raw
+      // accumulator) for the saved copy of EPI_GELU_SAVE.
+      auto item = [&](int i, int j, int qq, bool raw) {
+        float v0 = acc[i][j][4 * qq], v1 = acc[i][j][4 * qq + 1];
+        float v2 = acc[i][j][4 * qq + 2], v3 = acc[i][j][4 * qq + 3];
+        if (!raw) {
+          if constexpr (EPI == EPI_GELU_TANH || EPI == EPI_GELU_SAVE) {
+            v0 = gelu_tanh_fast(v0); v1 = gelu_tanh_fast(v1);
+            v2 = gelu_tanh_fast(v2); v3 = gelu_tanh_fast(v3);
+          }
+          if constexpr (EPI == EPI_GELU_BWD) {
+            const uint2 p = pre[i][j][qq];
+            v0 *= gelu_tanh_grad_fast(__uint_as_float(p.x << 16));
+            v1 *= gelu_tanh_grad_fast(__uint_as_float(p.x & 0xFFFF0000u));
+            v2 *= gelu_tanh_grad_fast(__uint_as_float(p.y << 16));
+            v3 *= gelu_tanh_grad_fast(__uint_as_float(p.y & 0xFFFF0000u));
+          }
+        }
+        uint2 u;
+        u.x = pack_bf16x2(v0, v1);
+        u.y = pack_bf16x2(v2, v3);
+        return u;
+      };
+      if constexpr (STAGED) {
+        // Through LDS: a lane's items cover 16 bytes of each of 32 rows, so stored directly
+        // every store instruction would touch 32 rows with 16 bytes each.  Row block i of the
+        // wave is written to its LDS block in that layout and read back as whole 16-byte
+        // chunks, 64 / ECH rows per instruction, so each global store writes 64 / ECH rows of
+        // WN * 2 contiguous bytes.  Chunk c of staged row r sits at chunk (c + r) mod ECH,
+        // which spreads a write's 32 rows over the LDS banks.  The block is private to the
+        // wave and its LDS accesses execute in order, so no barrier is needed.
+        char* const ew = epi_smem + wv * (32 * EPITCH);
+        const int er = lane & 31, eh = lane >> 5;
+        constexpr int RPI_E = 64 / ECH;
+        const int rr = lane / ECH, ch = lane % ECH;
+        auto staged = [&](int i, bool raw, void* dst, int64_t ld) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int64_t row = row0 + 32 * i;
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+            for (int qq = 0; qq < 4; ++qq) {
+              const int c = (4 * j + qq + er) & (ECH - 1);
+              *(uint2*)(ew + er * EPITCH + c * 16 + eh * 8) = item(i, j, qq, raw);
+            }
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int64_t col = col0 + 32 * j + 8 * qq;
-            if (row < M && col < N) {
-              float v0 = acc[i][j][4 * qq], v1 = acc[i][j][4 * qq + 1];
-              float v2 = acc[i][j][4 * qq + 2], v3 = acc[i][j][4 * qq + 3];
-              if constexpr (EPI == EPI_GELU_SAVE) {
-                uint2 u;
-                u.x = pack_bf16x2(v0, v1);
-                u.y = pack_bf16x2(v2, v3);
-                *(uint2*)((bf16_t*)g.aux + row * g.ldaux + col) = u;
+          for (int it = 0; it < 32 / RPI_E; ++it) {
+            const int r = it * RPI_E + rr;
+            const uint4 v = *(const uint4*)(ew + r * EPITCH + ((ch + r) & (ECH - 1)) * 16);
+            const int64_t row = m_w + 32 * i + r, col = n_w + 8 * ch;
+            if (row < M && col < N) *(uint4*)((bf16_t*)dst + row * ld + col) = v;
+          }
+        };
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if constexpr (EPI == EPI_GELU_SAVE) staged(i, true, g.aux, g.ldaux);
+          staged(i, false, g.C, ldc);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int64_t row = row0 + 32 * i;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const int64_t col = col0 + 32 * j + 8 * qq;
+              if (row < M && col < N) {
+                if constexpr (EPI == EPI_GELU_SAVE)
+                  *(uint2*)((bf16_t*)g.aux + row * g.ldaux + col) = item(i, j, qq, true);
+                *(uint2*)((bf16_t*)g.C + row * ldc + col) = item(i, j, qq, false);
               }
-              if constexpr (EPI == EPI_GELU_TANH || EPI == EPI_GELU_SAVE) {
-                v0 = gelu_tanh_fast(v0); v1 = gelu_tanh_fast(v1);
-                v2 = gelu_tanh_fast(v2); v3 = gelu_tanh_fast(v3);
-              }
-              if constexpr (EPI == EPI_GELU_BWD) {
-                const uint2 p = pre[i][j][qq];
-                v0 *= gelu_tanh_grad_fast(__uint_as_float(p.x << 16));
-                v1 *= gelu_tanh_grad_fast(__uint_as_float(p.x & 0xFFFF0000u));
-                v2 *= gelu_tanh_grad_fast(__uint_as_float(p.y << 16));
-                v3 *= gelu_tanh_grad_fast(__uint_as_float(p.y & 0xFFFF0000u));
-              }
-              uint2 u;
-              u.x = pack_bf16x2(v0, v1);
-              u.y = pack_bf16x2(v2, v3);
-              *(uint2*)((bf16_t*)g.C + row * ldc + col) = u;
             }
           }
         }
@@ -714,10 +762,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
               if (row < M && col < N) ((float*)g.C)[row * ldc + col] = old[j][r] + acc[i][j][r];
             }
           } else {
+            // Streaming stores: a partial is read once, by a later kernel, and a product's
+            // partials outgrow every cache level; dirty lines left in the Infinity Cache would
+            // be written back during the reduce that reads the partials (on MI355X these stores
+            // take the reduce after the product from 730 to 712 us, and the product itself
+            // from 913 to 907 us).
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int64_t row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
-              if (row < M && col < N) ((float*)g.C)[row * ldc + col] = acc[i][j][r];
+              if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][r], (float*)g.C + row * ldc + col);
             }
           }
         }

@@ -7,12 +7,13 @@
 //
 // HBM-bound.  One workgroup per row at a time; each thread owns NCH runs of 8 consecutive elements
 // (32 bytes of every fp32 partial, 16 bytes of a bf16 row), spaced THREADS runs apart so a
-// wave's loads are contiguous.  Loads go out in batches: for each partial in turn every
-// run's loads (NCH 32-byte loads per thread), issued while the previous partial is being
-// added; then the residual row; then gamma and beta ahead of the statistics.  The partials
-// are read once and the outputs written once, so those accesses are streaming
-// (non-temporal): on MI355X that moves the fused reduce from 4.9 to 5.45 TB/s.  A
-// streaming residual load measured slower and is not used.
+// wave's loads are contiguous.  The partials are read in two alternating register batches
+// (partial p+1 in flight while p is added); then the residual row; then gamma and beta ahead
+// of the statistics.  The partials are read once and the outputs written once, so those
+// accesses are streaming (non-temporal): on MI355X that moves the fused reduce from 4.9 to
+// 5.45 TB/s.  A streaming residual load measured slower and is not used, and so did every
+// other cache policy of the output stores.  With the stores left out the same kernel reads
+// at 6.5 TB/s; the 0.4 GB of h and y it writes cost about a fifth of its time.
 // The row stays in registers: the mean is a wave shuffle reduction plus one cross-wave step
 // through LDS, and the variance is a second pass over the registers (no E[x^2] - mean^2).
 #include "common.hpp"
@@ -39,6 +40,9 @@ struct F8 {
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// Cache policy of a buffer load: non-temporal (streaming; the partials are read once).
+constexpr int CPOL_NT = 2;
 
 // 8 consecutive elements of a bf16 or fp32 output row, written as streaming stores.
 template <bool BF16>
@@ -107,48 +111,70 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
 
     bool in[NCH];
     int64_t col[NCH];
+    uint32_t boff[NCH];  // byte offset of the run in an fp32 row (past the row: out of range)
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       col[c] = ((int64_t)c * THREADS + tid) * 8;
       in[c] = FULL || col[c] < H;
+      boff[c] = (uint32_t)col[c] * 4u;
     }
 
-    // h = sum of the partials in ascending order, then + residual.  The loads of partial p+1
-    // go out before partial p is added, so a batch is always in flight.
+    // h = sum of the partials in ascending order, then + residual.  Two register batches
+    // alternate: the loads of partial p+1 go out before partial p is added, so one batch is
+    // always in flight while the other is summed.  The loads are buffer loads from a resource
+    // spanning the row of one partial (wave-uniform, in scalar registers), at per-lane byte
+    // offsets shared by all partials.  The loop body has no branch: a conditional use of a
+    // batch lets the compiler sink its loads behind the next batch's and wait for both; the
+    // last one or two partials are summed after it.
     float v[NCH][8];
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+    const int np = r.n_parts;
     auto load_part = [&](int p, f32x4_t (&q)[NCH][2]) {
       const float* part = r.parts + (int64_t)p * r.part_stride + roff;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, (int)(H * 4), 0x00020000);
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        if (in[c]) {
-          q[c][0] = __builtin_nontemporal_load((const f32x4_t*)(part + col[c]));
-          q[c][1] = __builtin_nontemporal_load((const f32x4_t*)(part + col[c] + 4));
-        } else {
-          q[c][0] = q[c][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, CPOL_NT));
+        q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, CPOL_NT));
       }
     };
-    if (r.n_parts > 0) {
-      f32x4_t qa[NCH][2], qb[NCH][2];
-      load_part(0, qa);
-      for (int p = 0; p < r.n_parts; ++p) {
-        if (p + 1 < r.n_parts) load_part(p + 1, qb);
+    auto add_part = [&](const f32x4_t (&q)[NCH][2]) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
+      for (int c = 0; c < NCH; ++c)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[c][e] += qa[c][0][e];
-            v[c][4 + e] += qa[c][1][e];
-          }
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          qa[c][0] = qb[c][0];
-          qa[c][1] = qb[c][1];
+        for (int e = 0; e < 4; ++e) {
+          v[c][e] += q[c][0][e];
+          v[c][4 + e] += q[c][1][e];
         }
+    };
+    if (np > 0) {
+      f32x4_t qa[NCH][2], qb[NCH][2];
+      // The scheduling barriers keep each batch's loads ahead of the previous batch's adds
+      // (the scheduler would otherwise move the adds up and wait with nothing in flight).
+      load_part(0, qa);
+      int p = 0;
+      for (; p + 2 < np; p += 2) {
+        load_part(p + 1, qb);
+        __builtin_amdgcn_sched_barrier(0);
+        add_part(qa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_part(p + 2, qa);
+        __builtin_amdgcn_sched_barrier(0);
+        add_part(qb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (p + 1 < np) {
+        load_part(p + 1, qb);
+        __builtin_amdgcn_sched_barrier(0);
+        add_part(qa);
+        __builtin_amdgcn_sched_barrier(0);
+        add_part(qb);
+      } else {
+        add_part(qa);
       }
     }
     Raw8<BF16> res[NCH];
