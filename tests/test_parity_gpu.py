@@ -381,6 +381,43 @@ def test_row_edge_shapes(lib, dtype, T, K, N, world, rank):
     check("row partial", Z, O.row_linear_partial(Xv[:, :K], Wv, rank, world), dtype)
 
 
+@pytest.mark.parametrize("T,H,nl,tile", [
+    (8190, 136, 1016, "256x128"),  # 32 x 8 tiles of 256 x 128, ragged rows and columns
+    (8190, 136, 1528, "256x192"),  # 32 x 8 tiles of 256 x 192
+    (8190, 136, 2040, "256x256"),  # 32 x 8 tiles of 256 x 256
+])
+@pytest.mark.parametrize("mode", ["none", "gelu", "save"])
+def test_column_tile_widths(lib, T, H, nl, tile, mode):
+    """Every bf16 column epilogue (plain, GeLU, GeLU keeping the pre-activation) at each tile
+    width the launch planner picks on 256 compute units, with ragged last rows, columns and
+    K, rank 1 of 2 and a leading dimension past the shard width.  The 256 x 128 and 256 x 256
+    tiles write their outputs through LDS, the 256 x 192 tile directly."""
+    tp, pl = lib
+    world, rank = 2, 1
+    N = world * nl
+    rng = np.random.Generator(np.random.PCG64(T + nl))
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((H, N)) / np.sqrt(H)).astype(np.float32)
+    Xd, Wd = dev_values(X, "bf16"), dev_values(W, "bf16")
+    Xv, Wv = host(Xd), host(Wd)
+    ld = nl + 8
+    Y = torch.full((T, ld), float("nan"), dtype=torch.bfloat16, device=Xd.device)
+    U = torch.full((T, ld), float("nan"), dtype=torch.bfloat16, device=Xd.device)
+    say(f"  column tile widths T={T} H={H} N/P={nl} ({tile} tiles) mode={mode}")
+    if mode == "save":
+        tp.tp_col_linear_gelu_save(Xd, Wd, Y, ld, U, ld, T, H, N, rank, world, tp.TP_BF16)
+    else:
+        act = tp.TP_ACT_GELU_TANH if mode == "gelu" else tp.TP_ACT_NONE
+        tp.tp_col_linear_gelu(Xd, Wd, Y, ld, T, H, N, rank, world, act, tp.TP_BF16)
+    _sync()
+    act = "none" if mode == "none" else "gelu_tanh"
+    check("column", Y[:, :nl], O.col_linear(Xv, Wv, rank, world, act), "bf16")
+    assert torch.isnan(Y[:, nl:].float()).all(), "column wrote past its shard width"
+    if mode == "save":
+        check("pre-activation", U[:, :nl], O.col_linear(Xv, Wv, rank, world), "bf16")
+        assert torch.isnan(U[:, nl:].float()).all(), "pre-activation written past its width"
+
+
 def test_column_split_launch(lib):
     """A product whose columns the launcher splits over two launches: 4096 columns of
     256 x 256 tiles (one full round on 256 compute units) and a 512-wide strip of 128 x 128
