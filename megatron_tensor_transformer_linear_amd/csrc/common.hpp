@@ -62,6 +62,11 @@ struct GemmDesc {
   int layout = LAY_NN;
   void* aux = nullptr;
   int64_t ldaux = 0;
+  // Split of the contraction (EPI_PARTIAL_F32 in LAY_NN only): work item s of a tile
+  // contracts k in [s K / ksplit, (s + 1) K / ksplit) and writes its fp32 partial at
+  // C + s * c_split_stride.  K / ksplit must be a multiple of 8.
+  int ksplit = 1;
+  int64_t c_split_stride = 0;
 };
 
 // Causal / full attention over one rank's heads.
@@ -89,6 +94,7 @@ struct ReduceDesc {
   void* y_out;
   int64_t rows, H;
   int bf16;  // io dtype is bf16 (else fp32)
+  int64_t ld_out = 0;  // row pitch of h_out and y_out in elements (0: H)
 };
 
 // Tile shapes of one bf16 product: columns [0, n0) with bm0 x bn0 tiles, then, if n1 > 0,
@@ -102,6 +108,15 @@ struct GemmPlan {
 GemmPlan gemm_bf16_plan(int64_t M, int64_t N, int cus);
 
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream);
+// Compute units of the current device (cached per device; 256 when it cannot be queried).
+int device_cus();
+// Workspace bytes launch_gemm_bf16_split needs for an M x N product: the fp32 partials of the
+// narrow strip of the launch plan (0 when the plan has no strip).
+int64_t gemm_bf16_split_workspace(int64_t M, int64_t N, int64_t K);
+// launch_gemm_bf16 for a plain bf16 store (EPI_STORE, LAY_NN), with the plan's narrow strip
+// computed as 256 x 256 tiles over KSPLIT contraction ranges into `ws` and summed into C by the
+// reduce kernel; without a strip (or when K does not split) it is launch_gemm_bf16.
+hipError_t launch_gemm_bf16_split(const GemmDesc& g, float* ws, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmDesc& g, hipStream_t stream);
 hipError_t launch_attention(const AttnDesc& a, hipStream_t stream);
 hipError_t launch_reduce_ln(const ReduceDesc& r, hipStream_t stream);

@@ -93,4 +93,59 @@ hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream) {
   return launch_plan(gemm_bf16_plan(g.M, g.N, device_cus()), g, stream);
 }
 
+// Split of the narrow strip's contraction.  The strip of a plan is the columns that do not
+// fill a whole round of 256 x 256 tiles; as 128 x 128 tiles it runs at half the rate of the
+// wide part (each 128 x 128 tile does a quarter of the MFMA work per K step for half the
+// loads).  Computed instead as 256 x 256 tiles over KSPLIT contraction ranges, the strip's
+// tiles times KSPLIT fill the compute units (the 8192 x 512 strip of the block's QKV
+// projection: 64 tiles x 4 = 256 work items), and the reduce kernel sums the fp32 partials
+// in split order into the bf16 output.
+namespace {
+constexpr int KSPLIT = 4;
+
+bool split_applies(const GemmPlan& pl, int64_t K) {
+  return pl.n1 > 0 && pl.bm1 == 128 && K % (KSPLIT * 8) == 0;
+}
+}  // namespace
+
+int64_t gemm_bf16_split_workspace(int64_t M, int64_t N, int64_t K) {
+  const GemmPlan pl = gemm_bf16_plan(M, N, device_cus());
+  return split_applies(pl, K) ? (int64_t)KSPLIT * M * pl.n1 * 4 : 0;
+}
+
+hipError_t launch_gemm_bf16_split(const GemmDesc& g, float* ws, hipStream_t stream) {
+  const GemmPlan pl = gemm_bf16_plan(g.M, g.N, device_cus());
+  if (!ws || !split_applies(pl, g.K) || g.epi != EPI_STORE || g.layout != LAY_NN)
+    return launch_plan(pl, g, stream);
+  GemmDesc a = g;
+  a.N = pl.n0;
+  hipError_t e = launch_shape(pl.bm0, pl.bn0, a, stream);
+  if (e != hipSuccess) return e;
+  GemmDesc b = g;  // the strip: KSPLIT fp32 partials [M, n1], dense, one after another
+  b.N = pl.n1;
+  b.n_off = g.n_off + pl.n0;
+  b.C = ws;
+  b.ldc = pl.n1;
+  b.epi = EPI_PARTIAL_F32;
+  b.ksplit = KSPLIT;
+  b.c_split_stride = g.M * pl.n1;
+  e = launch_shape(256, 256, b, stream);
+  if (e != hipSuccess) return e;
+  ReduceDesc r;
+  r.parts = ws;
+  r.n_parts = KSPLIT;
+  r.part_stride = g.M * pl.n1;
+  r.residual = nullptr;
+  r.gamma = nullptr;
+  r.beta = nullptr;
+  r.eps = 0.0f;
+  r.h_out = (bf16_t*)g.C + pl.n0;
+  r.y_out = nullptr;
+  r.rows = g.M;
+  r.H = pl.n1;
+  r.bf16 = 1;
+  r.ld_out = g.ldc;
+  return launch_reduce_ln(r, stream);
+}
+
 }  // namespace tpk

@@ -54,9 +54,6 @@
 
 namespace tpk {
 
-// Compute units of the current device (the persistent grid size), cached per device.
-int device_cus();
-
 // Launch one product with BM x BN tiles (bm 128 implies bn 128) in layout g.layout.  An
 // epilogue the layout is not built for returns hipErrorInvalidValue.
 hipError_t launch_shape_nn(int bm, int bn, const GemmDesc& g, hipStream_t stream);
@@ -268,8 +265,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
 
   const int64_t M = g.M, N = g.N, K = g.K;
   const int tm = (int)((M + BM - 1) / BM), tn = (int)((N + BN - 1) / BN);
-  const int nt = tm * tn;
-  const int nk = (int)((K + BK - 1) / BK);
+  // Work items: split s of output tile i is item s * ntile + i (ksplit is 1 unless the
+  // launcher splits the contraction); an item contracts Kc consecutive k from s * Kc.
+  const int ntile = tm * tn;
+  const int nt = ntile * g.ksplit;
+  const int64_t Kc = K / g.ksplit;
+  const int nk = (int)((Kc + BK - 1) / BK);
   const int ng = (nk + NST - 1) / NST;  // groups of NST K steps per tile (last one padded)
 
   const bf16_t* __restrict__ A = (const bf16_t*)g.A;
@@ -287,6 +288,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
     i32x4_t rsrc_a, rsrc_b;
     uint32_t a_off[A_LD];
     uint32_t b_off[B_LD];
+    int kb;  // first k of the item's contraction range
   };
   // Row and first k (relative to the stage or pair) of lane `lane`'s 16 bytes in load
   // instruction i of a K-contiguous operand (PR: paired).
@@ -311,12 +313,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       off[i] = ((uint32_t)kc_row(SC, PC, i) * ld32 + (uint32_t)kc_k(SC, PC, i)) * 2u;
   };
   auto tile_loads = [&](int t, TileLoads& d) {
-    int tile_m = 0, tile_n = 0;
+    int tile_m = 0, tile_n = 0, ks = 0;
     const bool live = t < nt;
-    if (live) tile_coords(t, tm, tn, tile_m, tile_n);
+    if (live) {
+      ks = t / ntile;
+      tile_coords(t - ks * ntile, tm, tn, tile_m, tile_n);
+    }
+    d.kb = (int)(ks * Kc);
     const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
     if constexpr (A_KC) {
-      kc_loads(SA{}, std::integral_constant<bool, A_PAIR>{}, A + m0 * lda,
+      kc_loads(SA{}, std::integral_constant<bool, A_PAIR>{}, A + m0 * lda + d.kb,
                live ? min((int64_t)BM, M - m0) : 0, lda, d.rsrc_a, d.a_off);
     } else {
 #pragma unroll
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       }
     }
     if constexpr (B_KC) {
-      kc_loads(SB{}, std::integral_constant<bool, B_PAIR>{}, B + (g.n_off + n0) * ldb,
+      kc_loads(SB{}, std::integral_constant<bool, B_PAIR>{}, B + (g.n_off + n0) * ldb + d.kb,
                live ? min((int64_t)BN, N - n0) : 0, ldb, d.rsrc_b, d.b_off);
     } else {
 #pragma unroll
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   // K-contiguous operand's k bound is tested per lane, in a step (or pair) that reaches past K
   // (the test is wave-uniform otherwise), and only in loads issued in the last two groups of
   // K steps of a tile (CHK): an earlier load's stage ends at or before K.
-  const int Ki = (int)K;                       // K < 2^31 (bounded by the leading dimensions)
+  const int Ki = (int)Kc;                      // K < 2^31 (bounded by the leading dimensions)
   const int lda2 = (int)(lda * 2), ldb2 = (int)(ldb * 2);  // bytes per stored row
   const char* const Abytes = (const char*)A;
   const char* const Bbytes = (const char*)B;
@@ -463,7 +469,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         dma16<BUF * STAGE + U * 1024>(lds_a, off, d.rsrc_a, (uint32_t)k0 * 2u);
       } else {
         const int k_rows = max(0, min(BK, Ki - k0));
-        const i32x4_t rsrc = buffer_rsrc(Abytes + (int64_t)k0 * lda2, (int64_t)(k_rows * lda2));
+        const i32x4_t rsrc = buffer_rsrc(Abytes + (int64_t)(d.kb + k0) * lda2, (int64_t)(k_rows * lda2));
         dma16<BUF * STAGE + U * 1024>(lds_a, d.a_off[U], rsrc, 0u);
       }
     } else {
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
         dma16<BUF * STAGE + I * 1024>(lds_b, off, d.rsrc_b, (uint32_t)k0 * 2u);
       } else {
         const int k_rows = max(0, min(BK, Ki - k0));
-        const i32x4_t rsrc = buffer_rsrc(Bbytes + (int64_t)k0 * ldb2, (int64_t)(k_rows * ldb2));
+        const i32x4_t rsrc = buffer_rsrc(Bbytes + (int64_t)(d.kb + k0) * ldb2, (int64_t)(k_rows * ldb2));
         dma16<BUF * STAGE + I * 1024>(lds_b, d.b_off[I], rsrc, 0u);
       }
     }
@@ -631,9 +637,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       });
     }
 
-    // Epilogue of tile t (see the accumulator layout above).
+    // Epilogue of item t (see the accumulator layout above).
     int tile_m, tile_n;
-    tile_coords(t, tm, tn, tile_m, tile_n);
+    const int ks = t / ntile;
+    tile_coords(t - ks * ntile, tm, tn, tile_m, tile_n);
     const int64_t m_w = (int64_t)tile_m * BM + wm * WM, n_w = (int64_t)tile_n * BN + wn * WN;
     if constexpr (TRANS) {
       const int64_t row0 = m_w + (lane & 31), col0 = n_w + 4 * (lane >> 5);
@@ -736,6 +743,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
       }
     } else {
       const int64_t row0 = m_w + 4 * (lane >> 5), col0 = n_w + (lane & 31);
+      float* const Cs = (float*)g.C + (int64_t)ks * g.c_split_stride;  // this split's partial
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         // EPI_ACC_F32: row block i's previous values in one batch of loads, then the stores
@@ -770,7 +778,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int64_t row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
-              if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][r], (float*)g.C + row * ldc + col);
+              if (row < M && col < N) __builtin_nontemporal_store(acc[i][j][r], Cs + row * ldc + col);
             }
           }
         }
@@ -807,7 +815,7 @@ hipError_t launch_epi(dim3 grid, const GemmDesc& g, hipStream_t stream) {
 template <int BM, int BN, int NST, int LAY>
 hipError_t launch_tile(const GemmDesc& g, hipStream_t stream) {
   const int64_t tm = (g.M + BM - 1) / BM, tn = (g.N + BN - 1) / BN;
-  const int64_t tiles = tm * tn;
+  const int64_t tiles = tm * tn * g.ksplit;  // work items
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   // One workgroup per compute unit (each holds 64-128 KB of LDS), looping over tiles.

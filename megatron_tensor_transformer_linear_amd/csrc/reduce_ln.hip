@@ -107,7 +107,8 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   const int tid = threadIdx.x;
   for (int64_t row = blockIdx.x; row < r.rows; row += gridDim.x) {
     const int64_t H = r.H;
-    const int64_t roff = row * H;
+    const int64_t roff = row * H;                              // inputs: dense rows
+    const int64_t ooff = row * (r.ld_out > 0 ? r.ld_out : H);  // outputs: rows of pitch ld_out
 
     bool in[NCH];
     int64_t col[NCH];
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
           F8 o;
 #pragma unroll
           for (int e = 0; e < 8; ++e) o.v[e] = v[c][e];
-          store8<BF16>(r.h_out, roff + col[c], o);
+          store8<BF16>(r.h_out, ooff + col[c], o);
         }
       }
 #pragma unroll
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
         F8 y;
 #pragma unroll
         for (int e = 0; e < 8; ++e) y.v[e] = (v[c][e] - mean) * rstd * gv[e] + bv[e];
-        store8<BF16>(r.y_out, roff + col[c], y);
+        store8<BF16>(r.y_out, ooff + col[c], y);
       }
     }
   }  // row loop

@@ -28,7 +28,7 @@ inline int check_rank(int rank, int world) {
 inline int launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
 
 struct AttnSizes {
-  int64_t T, hl, nb, qkv_bytes, a_bytes, total;
+  int64_t T, hl, nb, qkv_bytes, a_bytes, split_bytes, total;
 };
 
 int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim, int world,
@@ -43,7 +43,10 @@ int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
   s->nb = s->hl * head_dim;
   s->qkv_bytes = s->T * 3 * s->nb * 2;
   s->a_bytes = s->T * s->nb * 2;
-  s->total = ((s->qkv_bytes + s->a_bytes) + 255) & ~(int64_t)255;
+  // fp32 partials of the QKV projection's narrow strip when its contraction is split (a
+  // device query: the strip depends on the compute-unit count)
+  s->split_bytes = gemm_bf16_split_workspace(s->T, 3 * s->nb, H);
+  s->total = ((s->qkv_bytes + s->a_bytes + s->split_bytes) + 255) & ~(int64_t)255;
   return TP_OK;
 }
 
@@ -100,6 +103,7 @@ int attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpa
 
   bf16_t* ws_qkv = (bf16_t*)workspace;
   bf16_t* ws_a = (bf16_t*)((char*)workspace + s.qkv_bytes);
+  float* ws_split = s.split_bytes ? (float*)((char*)workspace + s.qkv_bytes + s.a_bytes) : nullptr;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
 
@@ -119,7 +123,7 @@ int attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpa
   q.N = 3 * s.nb;
   q.K = H;
   q.epi = EPI_STORE;
-  if (launch_gemm_bf16(q, st) != hipSuccess) return TP_ERR_LAUNCH;
+  if (launch_gemm_bf16_split(q, ws_split, st) != hipSuccess) return TP_ERR_LAUNCH;
 
   AttnDesc a;
   a.qkv = ws_qkv;

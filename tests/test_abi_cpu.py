@@ -312,6 +312,15 @@ def test_workspace_bytes(tp):
     assert tp.tp_attn_workspace_bytes(2, 64, 1000, 8, 128, 4, tp.TP_BF16) == 0
 
 
+def test_workspace_bytes_split_strip(tp):
+    """The block's attention shard (8192 tokens, 12 heads per rank): its QKV projection's
+    launch plan on 256 compute units (the count assumed when no device can be queried) has a
+    512-wide strip, whose split contraction adds 4 fp32 partials of 8192 x 512 to the workspace."""
+    T, nb = 4 * 2048, (96 // 8) * 128
+    plain = (T * 3 * nb * 2 + T * nb * 2 + 255) // 256 * 256
+    assert tp.tp_attn_workspace_bytes(4, 2048, 12288, 96, 128, 8, tp.TP_BF16) == plain + 4 * T * 512 * 4
+
+
 def test_python_wrapper_raises(tp):
     with pytest.raises(tp.TPError) as e:
         tp.tp_col_linear_gelu(P, P, P, 512, 64, 256, 1024, 2, 2, 1, tp.TP_BF16, stream=0)

@@ -460,6 +460,39 @@ def test_row_dense_shard(lib, dtype, T, K, N, world, rank):
     check("row partial (dense shard)", Z, O.row_linear_partial(Xv, Wv, rank, world), dtype)
 
 
+def test_attention_qkv_split_strip(lib):
+    """The attention shard's QKV projection when its launch plan has a narrow strip (on 256
+    compute units: 8192 columns of 256 x 256 tiles plus a 256-wide strip): the strip's
+    contraction is split over 4 ranges into fp32 partials in the workspace and summed into
+    the bf16 QKV by the reduce kernel.  The QKV in the workspace and the output partial are
+    checked on sampled rows against the oracle."""
+    tp, pl = lib
+    batch, seq, nh, d, world, rank = 1, 2048, 22, 128, 1, 0
+    H = nh * d  # 2816: the rank's QKV is 2048 x 8448, contraction 2816
+    T = batch * seq
+    rng = np.random.Generator(np.random.PCG64(2816))
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    Wqkv = (rng.standard_normal((H, 3 * H)) / np.sqrt(H)).astype(np.float32)
+    Wo = (rng.standard_normal((H, H)) / np.sqrt(H)).astype(np.float32)
+    Xd, Wqd, Wod = dev_values(X, "bf16"), dev_values(Wqkv, "bf16"), dev_values(Wo, "bf16")
+    Xv, Wqv, Wov = host(Xd), host(Wqd), host(Wod)
+    plain = (T * 3 * H * 2 + T * H * 2 + 255) // 256 * 256
+    ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, H, nh, d, world, tp.TP_BF16)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert ws_bytes == plain + 4 * T * 256 * 4, "workspace has no room for the split strip"
+    sh = pl.AttnShard(Xd, Wqd, Wod, world, batch, seq, nh, d, True)
+    say(f"  attention QKV with a split strip T={T} H={H} heads={nh}")
+    sh.step()
+    _sync()
+    rows = sample_rows(T, seq, 5)
+    QKV, _ = sh.workspace_views()
+    lo, hi = O.head_range(nh, world, rank)
+    Wr = np.hstack([blk[:, lo * d:hi * d] for blk in O.split_qkv(Wqv, H)])
+    check("QKV (rows)", QKV[rows], O.matmul(Xv[rows], Wr), "bf16")
+    check("partial (rows)", sh.parts[rank][rows],
+          O.attn_head_shard(Xv, Wqv, Wov, nh, d, rank, world, batch, seq, True, rows), "bf16")
+
+
 @pytest.mark.parametrize("batch,seq,n_heads,world,causal", [
     (1, 1, 2, 1, True),        # one token
     (3, 65, 4, 2, True),       # one key past a key block, three sequences
