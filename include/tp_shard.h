@@ -24,7 +24,8 @@
  *   - Ranks are numbered 0..world-1; rank r owns block r of a split dimension, and rank 0
  *     owns the first block (typc.net section 2.1; pwwt.cn section 3.1).
  *   - Accumulation is always fp32.  bf16 results are rounded to nearest even.
- *   - Every argument is validated BEFORE any HIP call.  On error the call returns a
+ *   - Every argument is validated BEFORE any launch (the only HIP calls before it are
+ *     queries of the current device's compute-unit count).  On error the call returns a
  *     negative tp_status, launches nothing and leaves every output untouched.  A launch
  *     failure returns TP_ERR_LAUNCH.
  *   - Alignment: pointers 16-byte aligned; leading dimensions, shard widths and the
@@ -180,7 +181,10 @@ int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t
                            int64_t N, int rank, int world, int accumulate, int dtype,
                            void* stream);
 
-/* Workspace bytes tp_attn_head_shard needs for these sizes; 0 if the sizes are invalid. */
+/* Workspace bytes tp_attn_head_shard needs for these sizes on the current device; 0 if the
+ * sizes are invalid.  It queries the device's compute-unit count (the QKV projection's launch
+ * plan, and with it the size of the split-strip partials below, depends on it), so call it
+ * with the device current that the attention call will run on. */
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_heads,
                                int head_dim, int world, int dtype);
 
@@ -200,7 +204,11 @@ size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_head
  * visible to query i iff j <= i within the same sequence.  Only dtype TP_BF16.
  * workspace (device, >= tp_attn_workspace_bytes, 256-byte aligned) receives, as a
  * documented by-product, QKV_r bf16 [T, 3*hl*d] at offset 0 and A_r bf16 [T, hl*d] right
- * after it (offset T*3*hl*d*2 bytes).
+ * after it (offset T*3*hl*d*2 bytes).  When the QKV projection's launch plan has a narrow
+ * strip of columns (those that do not fill a whole round of 256 x 256 tiles on this device),
+ * the strip's contraction is split over 4 ranges whose fp32 partials follow A_r in the
+ * workspace and are summed in range order into QKV_r; the rest of QKV_r is one fp32
+ * accumulation per element.  Results are deterministic for a given device.
  * Errors: TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DIVISIBLE (n_heads % world), TP_ERR_RANK,
  * TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_LAUNCH. */
 int tp_attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,

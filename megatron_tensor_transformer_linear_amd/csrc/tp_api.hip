@@ -1,6 +1,7 @@
 // C ABI of the tensor-parallel layer-shard library: argument validation, shard-offset
-// arithmetic (64-bit integers) and kernel launches.  Every check runs before the first HIP
-// call, so an invalid call launches nothing and leaves its outputs untouched.
+// arithmetic (64-bit integers) and kernel launches.  Every check runs before the first
+// launch (the only earlier HIP calls query the device's compute-unit count), so an invalid
+// call launches nothing and leaves its outputs untouched.
 #include <math.h>
 
 #include "../../include/tp_shard.h"
