@@ -109,7 +109,9 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
     """Backward of the block's MLP pair (outside the timed forward step): every rank's four
     backward products, dY = dZ.W2_r^T with GeLU' fused, dW2_r = Y_r^T.dZ, dX_r = dU_r.W1_r^T,
     dW1_r = X^T.dU_r, then the reduce of the 8 input-gradient partials.  One untimed pass,
-    then two timed passes; each product is timed on its own with HIP events on its stream."""
+    then two timed passes; each kind of product runs for the 8 ranks back to back and is timed
+    as a group with HIP events on its stream at the group boundaries (per launch: the group's
+    time over 8)."""
     import torch
     from megatron_tensor_transformer_linear_amd import pipeline as pl
     from workloads import output_gradient
@@ -122,28 +124,26 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
             "dW2": lambda r: trn.backward_row(r, False, True),
             "dX_part": lambda r: trn.backward_col(r, True, False),
             "dW1": lambda r: trn.backward_col(r, False, True)}
-    ev = {k: [] for k in list(legs) + ["reduce_dX"]}
+    ev = {k: [] for k in list(legs) + ["reduce_dX", "pass"]}
+    # Each product runs for all ranks back to back (rank r's dX and dW1 read its dU_r, which
+    # its dY product wrote in an earlier group), with events only at the group boundaries.
     for it in range(3):
-        s0 = torch.cuda.Event(enable_timing=True)
+        s0 = prev = torch.cuda.Event(enable_timing=True)
         s0.record(stream)
-        for r in range(cfg.world):
-            for k, fn in legs.items():
-                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s_.record(stream)
+        for k, fn in legs.items():
+            for r in range(cfg.world):
                 fn(r)
-                e_.record(stream)
-                if it > 0:
-                    ev[k].append((s_, e_))
-        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_.record(stream)
+            e_ = torch.cuda.Event(enable_timing=True)
+            e_.record(stream)
+            if it > 0:
+                ev[k].append((prev, e_))
+            prev = e_
         trn.reduce_dx()
+        e_ = torch.cuda.Event(enable_timing=True)
         e_.record(stream)
         if it > 0:
-            ev["reduce_dX"].append((s_, e_))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        if it > 0:
-            ev.setdefault("pass", []).append((s0, e0))
+            ev["reduce_dX"].append((prev, e_))
+            ev["pass"].append((s0, e_))
     torch.cuda.synchronize()
     T, H, fl = cfg.tokens, cfg.hidden, cfg.ffn // cfg.world
     gemm_flops = 2.0 * T * H * fl  # each of the four products
@@ -151,7 +151,7 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
                    "dX partial (NT), dW1 (TN), reduce of the dX partials",
            "gemm_gflop_per_rank": round(4 * gemm_flops / 1e9, 1)}
     for k in legs:
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[k]]))
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) / cfg.world
         out[k] = {"avg_ms": round(ms, 4), "tflops": round(gemm_flops / ms / 1e9, 1)}
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev["reduce_dX"]]))
     nbytes = reduce_bytes(T, H, cfg.world, "bf16", residual=False, h_out=True, y_out=False)
@@ -176,28 +176,8 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
     fb = pl.BlockShard(blk.X, blk.Wqkv, blk.Wo, blk.W1, blk.W2, blk.g1, blk.b1, blk.g2, blk.b2,
                        cfg.world, cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, True, cfg.eps,
                        fold=True)
-    keys = ("pre_ln", "attn", "reduce1", "mlp_col", "mlp_row", "reduce2")
-    ev = {k: [] for k in keys}
-
-    def timed(key, fn, record):
-        if record:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            fn()
-            e.record(stream)
-            ev[key].append((s, e))
-        else:
-            fn()
-
-    def step(record):
-        timed("pre_ln", fb.pre_ln, record)
-        for r in range(cfg.world):
-            timed("attn", lambda r=r: fb.attn(r), record)
-        timed("reduce1", fb.reduce1, record)
-        for r in range(cfg.world):
-            timed("mlp_col", lambda r=r: fb.mlp_col(r), record)
-            timed("mlp_row", lambda r=r: fb.mlp_row(r), record)
-        timed("reduce2", fb.reduce2, record)
+    ev = {k: [] for k in LAUNCHES}
+    step = stage_step(cfg, fb, stream, ev)
 
     step(False)
     torch.cuda.synchronize()
@@ -212,8 +192,8 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
     r1 = reduce_bytes(T, H, 1, "bf16", residual=True, h_out=True, y_out=True)
     r2 = reduce_bytes(T, H, 1, "bf16", residual=True, h_out=True, y_out=False)
 
-    def avg_ms(key):
-        return float(np.mean([s.elapsed_time(e) for s, e in ev[key]]))
+    def avg_ms(key):  # per launch
+        return float(np.mean([s.elapsed_time(e) for s, e in ev[key]])) / LAUNCHES[key]
 
     out = {
         "what": ("the block step with each epilogue's reduce folded into the row-parallel "
@@ -233,6 +213,44 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
     del fb
     torch.cuda.empty_cache()
     return out
+
+
+# Calls per step of each stage: the attention-head shard, the column GEMM and the row GEMM run
+# once per simulated rank, the LayerNorm and the two reduces once.
+LAUNCHES = {"pre_ln": 1, "attn": 8, "reduce1": 1, "mlp_col": 8, "mlp_row": 8, "reduce2": 1}
+
+
+def stage_step(cfg, blk, stream, ev):
+    """One block step as stages, with a HIP event at each stage boundary when recording: the
+    pre-LayerNorm, the 8 ranks' attention-head shards, the first reduce, the 8 ranks' MLP
+    column GEMMs, their 8 row GEMMs, the second reduce.  The MLP runs all ranks' column
+    products, then all their row products (the ranks are independent; each rank's hidden
+    block stays in its own buffer).  An event recorded between two kernels holds the second
+    back for several microseconds on MI355X (a step with an event pair around every call had
+    about 270 us of idle gaps), so a step records 7 events: each stage's interval covers its
+    launches back to back, and a per-launch time is that interval over the launch count."""
+    import torch
+    assert cfg.world == LAUNCHES["attn"]
+    stages = (("pre_ln", lambda: blk.pre_ln()),
+              ("attn", lambda: [blk.attn(r) for r in range(cfg.world)]),
+              ("reduce1", lambda: blk.reduce1()),
+              ("mlp_col", lambda: [blk.mlp_col(r) for r in range(cfg.world)]),
+              ("mlp_row", lambda: [blk.mlp_row(r) for r in range(cfg.world)]),
+              ("reduce2", lambda: blk.reduce2()))
+
+    def step(record: bool):
+        prev = None
+        if record:
+            prev = torch.cuda.Event(enable_timing=True)
+            prev.record(stream)
+        for key, fn in stages:
+            fn()
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev[key].append((prev, e))
+                prev = e
+    return step
 
 
 def main() -> int:
@@ -288,27 +306,9 @@ def main() -> int:
     log("inputs resident in HBM")
 
     stream = torch.cuda.current_stream()
-    ev = {k: [] for k in ("pre_ln", "attn", "reduce1", "mlp_col", "mlp_row", "reduce2")}
-
-    def timed(key, fn, record):
-        if record:
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            fn()
-            e.record(stream)
-            ev[key].append((s, e))
-        else:
-            fn()
-
-    def step(record: bool):
-        timed("pre_ln", blk.pre_ln, record)
-        for r in range(cfg.world):
-            timed("attn", lambda r=r: blk.attn(r), record)
-        timed("reduce1", blk.reduce1, record)
-        for r in range(cfg.world):
-            timed("mlp_col", lambda r=r: blk.mlp_col(r), record)
-            timed("mlp_row", lambda r=r: blk.mlp_row(r), record)
-        timed("reduce2", blk.reduce2, record)
+    stage_keys = ("pre_ln", "attn", "reduce1", "mlp_col", "mlp_row", "reduce2")
+    ev = {k: [] for k in stage_keys}
+    step = stage_step(cfg, blk, stream, ev)
 
     for i in range(args.warmup):
         step(False)
@@ -322,8 +322,8 @@ def main() -> int:
     elapsed = time.perf_counter() - t_start
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
 
-    def avg_ms(key):
-        return float(np.mean([s.elapsed_time(e) for s, e in ev[key]]))
+    def avg_ms(key):  # per launch: the stage's event interval over its launches
+        return float(np.mean([s.elapsed_time(e) for s, e in ev[key]])) / LAUNCHES[key]
 
     fl = rank_flops(cfg)
     step_flops = cfg.world * sum(fl.values())
@@ -340,7 +340,7 @@ def main() -> int:
     stages = {}
     for key in ev:
         ms = avg_ms(key)
-        entry = {"avg_ms": round(ms, 4), "launches_per_step": len(ev[key]) // args.steps}
+        entry = {"avg_ms": round(ms, 4), "launches_per_step": LAUNCHES[key]}
         if key == "attn":
             entry["tflops"] = round((fl["qkv"] + fl["attn_core"] + fl["o_proj"]) / ms / 1e9, 1)
         elif key in ("mlp_col", "mlp_row"):
@@ -390,16 +390,16 @@ def main() -> int:
     # partials over its 1024 rows, fused with the residual add and LayerNorm, into its rows of
     # the full buffers (the all-gather).  Same kernel as reduce1, on a row range.
     sp_ev = []
-    for it in range(3):
+    for it in range(3):  # the 8 ranks back to back, timed as a group
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
         for r in range(cfg.world):
-            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s_.record(stream)
             blk.reduce1_scatter(r)
-            e_.record(stream)
-            if it > 0:
-                sp_ev.append((s_, e_))
+        e_.record(stream)
+        if it > 0:
+            sp_ev.append((s_, e_))
     torch.cuda.synchronize()
-    sp_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in sp_ev]))
+    sp_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in sp_ev])) / cfg.world
     sp_bytes = reduce_bytes(T // cfg.world, H, cfg.world, "bf16", residual=True, h_out=True,
                             y_out=True)
     result["sequence_parallel_epilogue"] = {

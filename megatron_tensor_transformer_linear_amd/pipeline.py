@@ -409,8 +409,12 @@ class BlockShard:
             self.attn(r)
 
     def mlp_phase(self):
+        # Every rank's column product, then every rank's row product: the ranks are
+        # independent and each keeps its hidden block in its own buffer, so the order changes
+        # no result (the folded row products still add in ascending rank order).
         for r in range(self.P):
             self.mlp_col(r)
+        for r in range(self.P):
             self.mlp_row(r)
 
     def step(self):
