@@ -494,6 +494,30 @@ def test_attention_qkv_split_strip(lib, seq):
           O.attn_head_shard(Xv, Wqv, Wov, nh, d, rank, world, batch, seq, True, rows), "bf16")
 
 
+def test_attention_qkv_split_strip_integer_exact(lib):
+    """Integer pin of the split strip: with X sparse in {-1, 0, 1} (8 nonzeros per row) and
+    Wqkv in {-2..2}, every partial of every contraction range and their sum are small
+    integers, exact in fp32 and in bf16, so the whole QKV of rank 1 of 2 (its head blocks of
+    [Wq | Wk | Wv] through the column-block map, strip included) equals the oracle bit for bit.
+    A wrong contraction range, split offset or partial slot shows up as a wrong integer."""
+    tp, pl = lib
+    batch, seq, nh, d, world, rank = 1, 2048, 44, 128, 2, 1
+    H = nh * d  # 5632; the rank's QKV is 2048 x 8448 (8192 columns + a 256-wide strip)
+    T = batch * seq
+    rng = np.random.Generator(np.random.PCG64(44))
+    X = integer_matrix(rng, (T, H), -1, 1, "bf16", nnz_per_row=8)
+    Wqkv = integer_matrix(rng, (H, 3 * H), -2, 2, "bf16")
+    Wo = integer_matrix(rng, (H, H), -1, 1, "bf16")
+    sh = pl.AttnShard(dev(X), dev(Wqkv), dev(Wo), world, batch, seq, nh, d, True)
+    say(f"  attention QKV split strip, integer inputs T={T} H={H} rank {rank}/{world}")
+    sh.rank(rank)
+    _sync()
+    QKV, _ = sh.workspace_views()
+    lo, hi = O.head_range(nh, world, rank)
+    Wr = np.hstack([blk[:, lo * d:hi * d] for blk in O.split_qkv(Wqkv.values(), H)])
+    check_exact("QKV (integer)", QKV, O.matmul(X.values(), Wr), "bf16")
+
+
 @pytest.mark.parametrize("batch,seq,n_heads,world,causal", [
     (1, 1, 2, 1, True),        # one token
     (3, 65, 4, 2, True),       # one key past a key block, three sequences
