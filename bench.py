@@ -22,7 +22,9 @@ the MLP pair (the four gradient products of every rank and the reduce of the inp
 partials; --no-backward skips it) are timed on their own and reported beside the step,
 outside `value`, and so is the same step with each epilogue's reduce folded into the
 row-parallel products (one fp32 running sum instead of 8 stacked partials; --no-fold skips
-it).
+it).  The other workloads of the path (the fp32 MLP, the single linear, the bf16 MLP shard and
+the attention-head shard) are timed the same way and reported per rank under
+`other_workloads` (--no-workloads skips them).
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ from workloads.configs import rank_flops, reduce_bytes  # noqa: E402
 WORKLOAD = "block_bf16_tp8"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_col_gelu_block_bf16_tp8_hbm_traffic.md")
@@ -253,6 +256,93 @@ def stage_step(cfg, blk, stream, ev):
     return step
 
 
+def other_workloads_leg(dev, steps: int = 5) -> dict:
+    """The other workloads of this path, each on its own and outside `value`: the fp32 MLP
+    (2 ranks, 64 tokens), the single linear (rank 0's column block and both row partials),
+    the bf16 MLP shard (4 ranks, 4096 tokens) and the attention-head shard (4 ranks, 16 heads
+    each).  Each stage runs for every rank back to back, with HIP events only at the stage
+    boundaries; 1 untimed step, then `steps` timed ones.  Per-rank times are a stage's
+    interval over its rank count."""
+    import torch
+    from megatron_tensor_transformer_linear_amd import pipeline as pl
+
+    stream = torch.cuda.current_stream()
+
+    def run(stages, n_steps):
+        ev = {k: [] for k, _ in stages}
+        for it in range(n_steps + 1):
+            prev = torch.cuda.Event(enable_timing=True)
+            prev.record(stream)
+            for key, fn in stages:
+                fn()
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                if it > 0:
+                    ev[key].append((prev, e))
+                prev = e
+        torch.cuda.synchronize()
+        return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+
+    out = {}
+    for name in ("mlp_f32_tp2", "linear_bf16_tp2", "mlp_bf16_tp4", "attn_bf16_tp4"):
+        cfg = get_config(name)
+        t = generate(cfg)
+        up = lambda a: pl.to_device(a.data, cfg.dtype, dev)  # noqa: E731
+        fl = rank_flops(cfg)
+        P, T, H = cfg.world, cfg.tokens, cfg.hidden
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+        if cfg.kind == "mlp":
+            sh = pl.MLPShard(up(t["X"]), up(t["A"]), up(t["B"]), P, cfg.dtype,
+                             gamma=up(t["gamma"]), beta=up(t["beta"]), eps=cfg.eps,
+                             residual_ln=cfg.dtype == "bf16")
+            ms = run((("column", lambda: [sh.column(r) for r in range(P)]),
+                      ("row", lambda: [sh.row(r) for r in range(P)]),
+                      ("reduce", sh.reduce)), steps)
+            shard_ms = (ms["column"] + ms["row"]) / P
+            rb = reduce_bytes(T, H, P, cfg.dtype, residual=sh.residual_ln, h_out=True,
+                              y_out=sh.residual_ln) if cfg.dtype == "bf16" else \
+                reduce_bytes(T, H, P, "f32", residual=False, h_out=True, y_out=False)
+            entry = {"shard_us_per_rank": round(shard_ms * 1e3, 2),
+                     "column_us": round(ms["column"] / P * 1e3, 2),
+                     "row_us": round(ms["row"] / P * 1e3, 2),
+                     "tflops_per_rank": round((fl["mlp_col"] + fl["mlp_row"]) / shard_ms / 1e9, 1),
+                     "reduce_us": round(ms["reduce"] * 1e3, 2),
+                     "reduce_gbs": round(rb / ms["reduce"] / 1e6, 1)}
+        elif cfg.kind == "linear":
+            sh = pl.LinearShard(up(t["X"]), up(t["W"]), P, cfg.dtype, col_ranks=(0,))
+            ms = run((("column", lambda: sh.column(0)),
+                      ("row", lambda: [sh.row(r) for r in range(P)]),
+                      ("reduce", sh.reduce)), steps)
+            rb = reduce_bytes(T, cfg.n_out, P, "f32", residual=False, h_out=True, y_out=False)
+            entry = {"column_rank0_us": round(ms["column"] * 1e3, 2),
+                     "column_tflops": round(fl["col"] / ms["column"] / 1e9, 1),
+                     "row_us_per_rank": round(ms["row"] / P * 1e3, 2),
+                     "row_tflops": round(fl["row"] / (ms["row"] / P) / 1e9, 1),
+                     "reduce_us": round(ms["reduce"] * 1e3, 2),
+                     "reduce_gbs": round(rb / ms["reduce"] / 1e6, 1)}
+            shard_ms = ms["column"]
+            entry["tflops_per_rank"] = entry["column_tflops"]
+        else:
+            qkv = np.ascontiguousarray(np.hstack([t["Wq"].data, t["Wk"].data, t["Wv"].data]))
+            sh = pl.AttnShard(up(t["X"]), pl.to_device(qkv, "bf16", dev), up(t["Wo"]), P,
+                              cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, cfg.causal)
+            ms = run((("shard", lambda: [sh.rank(r) for r in range(P)]),
+                      ("reduce", sh.reduce)), steps)
+            shard_ms = ms["shard"] / P
+            rb = reduce_bytes(T, H, P, "f32", residual=False, h_out=True, y_out=False)
+            entry = {"shard_us_per_rank": round(shard_ms * 1e3, 2),
+                     "tflops_per_rank": round((fl["qkv"] + fl["attn_core"] + fl["o_proj"]) /
+                                              shard_ms / 1e9, 1),
+                     "sum_of_partials_us": round(ms["reduce"] * 1e3, 2),
+                     "sum_of_partials_gbs": round(rb / ms["reduce"] / 1e6, 1)}
+        entry["pct_of_peak"] = round(100 * entry["tflops_per_rank"] / peak, 2)
+        out[name] = entry
+        del sh, t
+        torch.cuda.empty_cache()
+        log(f"workload {name} timed")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +351,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass measurement of the MLP pair")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the measurement of the other workloads (fp32 MLP, single linear, "
+                         "bf16 MLP shard, attention-head shard)")
     ap.add_argument("--no-fold", action="store_true",
                     help="skip the measurement of the step with folded reduces")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -411,6 +504,9 @@ def main() -> int:
     }
     if not args.no_backward:
         result["mlp_backward"] = mlp_backward_leg(cfg, t, blk, stream)
+    if not args.no_workloads:
+        log("timing the other workloads")
+        result["other_workloads"] = other_workloads_leg(dev)
     if not args.no_fold:
         log("timing the block step with folded reduces")
         result["folded_step"] = folded_block_leg(cfg, blk, stream, max(1, min(args.steps, 5)))
