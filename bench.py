@@ -223,6 +223,13 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
 LAUNCHES = {"pre_ln": 1, "attn": 8, "reduce1": 1, "mlp_col": 8, "mlp_row": 8, "reduce2": 1}
 
 
+def rank_shard(fl: dict, stages: dict) -> dict:
+    ms = stages["attn"]["avg_ms"] + stages["mlp_col"]["avg_ms"] + stages["mlp_row"]["avg_ms"]
+    tf = sum(fl.values()) / ms / 1e9
+    return {"ms": round(ms, 4), "gflop": round(sum(fl.values()) / 1e9, 1), "tflops": round(tf, 1),
+            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def stage_step(cfg, blk, stream, ev):
     """One block step as stages, with a HIP event at each stage boundary when recording: the
     pre-LayerNorm, the 8 ranks' attention-head shards, the first reduce, the 8 ranks' MLP
@@ -478,6 +485,11 @@ def main() -> int:
             "avg_launch_ms": round(col_ms, 4),
         },
         "stages": stages,
+        # One simulated rank's layer shard (its attention-head shard and its MLP shard), the
+        # unit the metric names: the rank's algorithmic flops over the sum of its stages'
+        # per-launch times (the reduces and the pre-LayerNorm are the all-reduce replacement
+        # and are left out here; `value` includes them).
+        "rank_shard": rank_shard(fl, stages),
     }
     # Sequence-parallel epilogue (outside the timed step): rank r's reduce-scatter of the 8
     # partials over its 1024 rows, fused with the residual add and LayerNorm, into its rows of
