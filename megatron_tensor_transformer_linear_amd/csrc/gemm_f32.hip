@@ -2,16 +2,18 @@
 // small fp32 MLP.  Same contract and epilogues as the bf16 tile (0539edu.com TP tutorial
 // section 1.1, formula 1.1 and figure 1.2), built on v_mfma_f32_16x16x4_f32.
 //
-// Tile 64 x 64 x 16, 256 threads = 4 waves in a 2 x 2 grid, each wave 32 x 32 as 2 x 2 blocks
+// Tile 64 x 64 x 64, 256 threads = 4 waves in a 2 x 2 grid, each wave 32 x 32 as 2 x 2 blocks
 // of 16 x 16.  Operand layout of the 16x16x4 instruction: A lane l holds A[l % 16][l / 16],
 // B lane l holds B[l / 16][l % 16]; accumulator element r of lane l is C[4 (l / 16) + r][l % 16].
-// These fp32 shapes are a few MFLOP, so the tile is single-buffered and launch-bound.
+// These fp32 shapes are a few MFLOP with few tiles, so the time is the chain of K steps: each
+// step's global loads go out before the previous step is multiplied (held in registers), and
+// the K step is 64 wide so a contraction of 512 takes 8 round trips to memory, not 32.
 #include "common.hpp"
 
 namespace tpk {
 namespace {
 
-constexpr int TM = 64, TN = 64, TK = 16;
+constexpr int TM = 64, TN = 64, TK = 64;
 constexpr int NT = 256;
 
 template <int EPI>
@@ -26,8 +28,9 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmDesc g) {
   const float* __restrict__ A = (const float*)g.A;
   const float* __restrict__ B = (const float*)g.B;
 
-  // A tile: thread -> row tid/4, k chunk (tid%4)*4.  B tile: k-row tid/16, n chunk (tid%16)*4.
-  const int a_r = tid >> 2, a_k = (tid & 3) * 4;
+  // A tile: thread -> rows tid/16 + 16 i, k chunk (tid%16)*4.  B tile: k-rows tid/16 + 16 i,
+  // n chunk (tid%16)*4 (i = 0..3).
+  const int a_r = tid >> 4, a_k = (tid & 15) * 4;
   const int b_r = tid >> 4, b_n = (tid & 15) * 4;
   const int64_t b_nlog = n0 + b_n;
   const bool b_nvalid = b_nlog < N;
@@ -39,19 +42,28 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmDesc g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  float4 ra[4], rb[4];  // the next K step's operands, in flight while the current is multiplied
+  auto gload = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = m0 + a_r + 16 * i, k = k0 + a_k;
+      ra[i] = (row < M && k < K) ? *(const float4*)(A + row * g.lda + k) : make_float4(0, 0, 0, 0);
+      const int64_t kb = k0 + b_r + 16 * i;
+      rb[i] = (b_nvalid && kb < K) ? *(const float4*)(B + kb * g.ldb + b_col) : make_float4(0, 0, 0, 0);
+    }
+  };
+  gload(0);
   for (int64_t k0 = 0; k0 < K; k0 += TK) {
-    {
-      const int64_t row = m0 + a_r, k = k0 + a_k;
-      float4 v = (row < M && k < K) ? *(const float4*)(A + row * g.lda + k) : make_float4(0, 0, 0, 0);
-      As[a_r][a_k + 0] = v.x;
-      As[a_r][a_k + 1] = v.y;
-      As[a_r][a_k + 2] = v.z;
-      As[a_r][a_k + 3] = v.w;
-      const int64_t kb = k0 + b_r;
-      float4 w = (b_nvalid && kb < K) ? *(const float4*)(B + kb * g.ldb + b_col) : make_float4(0, 0, 0, 0);
-      *(float4*)&Bs[b_r][b_n] = w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      As[a_r + 16 * i][a_k + 0] = ra[i].x;
+      As[a_r + 16 * i][a_k + 1] = ra[i].y;
+      As[a_r + 16 * i][a_k + 2] = ra[i].z;
+      As[a_r + 16 * i][a_k + 3] = ra[i].w;
+      *(float4*)&Bs[b_r + 16 * i][b_n] = rb[i];
     }
     __syncthreads();
+    if (k0 + TK < K) gload(k0 + TK);
 #pragma unroll
     for (int kk = 0; kk < TK; kk += 4) {
       float a[2], b[2];
