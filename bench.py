@@ -13,11 +13,15 @@ an FFN slice of 6144 each), batch 4 x seq 2048, causal, bf16 with fp32 accumulat
 
 Inputs are generated and resident in HBM before the timed region.  `value` is the whole
 step's algorithmic flops (all 8 ranks' shards) divided by the measured step time, in
-TFLOP/s.  Per-kernel durations come from HIP events recorded on the launch stream inside
-the timed region; the roofline object reports the dominant GEMM (the column-parallel
-GEMM + GeLU of the MLP).  The CPU baseline times the float64 oracle on a bounded row
-sample of the same workload on this host.  After the timed steps, the sequence-parallel
-form of the epilogue (each rank's reduce-scatter of its 1024 rows) and the backward pass of
+TFLOP/s, over steps run back to back.  Per-kernel durations come from HIP events recorded on
+the launch stream inside the timed region; the roofline object reports the kernel with the
+most time per step (one of the two MLP GEMMs), `rooflines` both.  The graphics and memory
+clocks are sampled through amdsmi during the timed steps, and the fractions of peak are also
+given at the measured graphics clock.  A cold-cache pass then times every stage again after
+writing 512 MiB of scratch (twice the 256 MB Infinity Cache) just before it, so nothing it
+reads is cached (`stages[*].cold_*`).  The CPU baseline times the float64 oracle on a bounded
+row sample of the same workload on this host, and the full oracle of each other workload.
+After the timed steps, the sequence-parallel form of the epilogue (each rank's reduce-scatter of its 1024 rows) and the backward pass of
 the MLP pair (the four gradient products of every rank and the reduce of the input-gradient
 partials; --no-backward skips it) are timed on their own and reported beside the step,
 outside `value`, and so is the same step with each epilogue's reduce folded into the
@@ -49,29 +53,137 @@ PEAK_HBM_GBS = 8000.0
 PEAK_F32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_col_gelu_block_bf16_tp8_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_block_bf16_tp8_hbm_traffic.md")
+FLUSH_MIB = 512  # scratch written before each cold-cache stage: 2x the 256 MB Infinity Cache
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per launch of the MLP column GEMM from the committed counter summary, or
-    None when the kernel sources no longer hash to the digest the counters were taken at."""
+def measured_traffic(role: str):
+    """HBM bytes per launch of one GEMM role ("mlp_col", "mlp_row") from the committed counter
+    summary (lines `traffic_bytes_per_launch.<role>: N`), or None when the kernel sources no
+    longer hash to the digest the counters were taken at."""
     import hashlib
     try:
-        kv = dict(l.split(": ", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ": " in l
-                  and l.split(": ", 1)[0] in ("kernel_sources", "kernel_sources_sha256",
-                                              "traffic_bytes_per_launch"))
+        kv = {}
+        for line in open(TRAFFIC_FILE).read().splitlines():
+            if ": " in line:
+                k, v = line.split(": ", 1)
+                kv[k.strip()] = v.strip()
         h = hashlib.sha256()
         for f in kv["kernel_sources"].split():
             h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest() != kv["kernel_sources_sha256"].strip():
+        if h.hexdigest() != kv["kernel_sources_sha256"]:
             return None
-        return int(kv["traffic_bytes_per_launch"])
+        return int(kv["traffic_bytes_per_launch." + role])
     except (OSError, KeyError, ValueError):
         return None
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (mean over its XCDs), memory clock and socket power
+    through amdsmi's GPU metrics every `period` seconds on a thread, between start() and
+    stop().  amdsmi reads the driver's metrics table; it makes no HIP call.  Any failure (no
+    amdsmi, no matching device) leaves the summary's `error` set instead of clocks."""
+
+    def __init__(self, period: float = 0.02):
+        import threading
+        self.period, self.samples, self.error = period, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            import torch
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            want = None
+            try:
+                p = torch.cuda.get_device_properties(0)
+                want = (int(p.pci_domain_id), int(p.pci_bus_id), int(p.pci_device_id))
+            except Exception:  # noqa: BLE001 - older torch: no PCI ids
+                pass
+            for h in handles:
+                if want is None:
+                    break
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._handle = h
+            if self._handle is None and len(handles) == 1:
+                self._handle = handles[0]
+            if self._handle is None:
+                self.error = f"no amdsmi device matched ({len(handles)} visible)"
+        except Exception as e:  # noqa: BLE001
+            self.error = f"amdsmi unavailable: {e}"
+
+    @staticmethod
+    def _num(v):
+        return float(v) if isinstance(v, (int, float)) and not isinstance(v, bool) else None
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        gfx = [self._num(v) for v in (m.get("current_gfxclks") or [])]
+        gfx = [v for v in gfx if v]
+        if not gfx and self._num(m.get("current_gfxclk")):
+            gfx = [self._num(m["current_gfxclk"])]
+        return (sum(gfx) / len(gfx) if gfx else None, self._num(m.get("current_uclk")),
+                self._num(m.get("current_socket_power")))
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # noqa: BLE001
+                self.error = f"amdsmi read failed: {e}"
+                return
+
+    def start(self):
+        if self._handle is None:
+            return
+        import threading
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self) -> dict:
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        out = {"source": "amdsmi GPU metrics (current_gfxclks averaged over the XCDs, "
+                         f"current_uclk, current_socket_power), every {self.period * 1e3:.0f} ms "
+                         "through the timed steps",
+               "samples": len(self.samples)}
+        if self.error:
+            out["error"] = self.error
+
+        def summary(i):
+            v = sorted(x[i] for x in self.samples if x[i] is not None)
+            if not v:
+                return None
+            return {"median": v[len(v) // 2], "mean": round(sum(v) / len(v), 1),
+                    "min": v[0], "max": v[-1]}
+        if self.samples:
+            out["sclk_mhz"] = summary(0)
+            out["mclk_mhz"] = summary(1)
+            out["socket_power_w"] = summary(2)
+        return out
+
+
+class CacheFlush:
+    """Writes FLUSH_MIB MiB of scratch (one fill kernel) on the current stream, evicting
+    everything a following kernel reads from the L2s and the 256 MB Infinity Cache."""
+
+    def __init__(self, dev, mib: int = FLUSH_MIB):
+        import torch
+        self.buf = torch.empty(mib << 18, dtype=torch.float32, device=dev)
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.buf.fill_(float(self.i))
 
 
 def cpu_baseline(cfg, t, qkv_vals) -> dict:
@@ -105,7 +217,8 @@ def cpu_baseline(cfg, t, qkv_vals) -> dict:
             "sample": (f"float64 oracle of the whole 8-rank block for {R} query rows "
                        f"({len(per_seq)} positions spread over 0..{S - 1} in each of the "
                        f"{cfg.batch} sequences; keys/values over the full causal prefixes): "
-                       f"{flops / 1e9:.0f} GFLOP in {dt:.1f} s")}
+                       f"{flops / 1e9:.0f} GFLOP in {dt:.1f} s; its matrix products are "
+                       "numpy float64 BLAS")}
 
 
 def mlp_backward_leg(cfg, t, blk, stream) -> dict:
@@ -223,11 +336,14 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
 LAUNCHES = {"pre_ln": 1, "attn": 8, "reduce1": 1, "mlp_col": 8, "mlp_row": 8, "reduce2": 1}
 
 
-def rank_shard(fl: dict, stages: dict) -> dict:
+def rank_shard(fl: dict, stages: dict, sclk_ghz=None) -> dict:
     ms = stages["attn"]["avg_ms"] + stages["mlp_col"]["avg_ms"] + stages["mlp_row"]["avg_ms"]
     tf = sum(fl.values()) / ms / 1e9
-    return {"ms": round(ms, 4), "gflop": round(sum(fl.values()) / 1e9, 1), "tflops": round(tf, 1),
-            "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    out = {"ms": round(ms, 4), "gflop": round(sum(fl.values()) / 1e9, 1), "tflops": round(tf, 1),
+           "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    if sclk_ghz:
+        out["pct_at_measured_sclk"] = round(100 * tf / (PEAK_BF16_TFLOPS * sclk_ghz / 2.4), 2)
+    return out
 
 
 def stage_step(cfg, blk, stream, ev):
@@ -263,24 +379,85 @@ def stage_step(cfg, blk, stream, ev):
     return step
 
 
-def other_workloads_leg(dev, steps: int = 5) -> dict:
+def cold_stages(cfg, blk, stream, flush, n_steps: int) -> dict:
+    """Each stage of the block step after a cache flush: per step, for every stage in order,
+    FLUSH_MIB MiB of scratch are written, then the stage runs between two events.  The stage's
+    first launch therefore finds nothing of its operands cached (later launches of a stage,
+    the 8 ranks back to back, see what the earlier ones left, as in the step).  Returns the
+    per-launch milliseconds of each stage, averaged over n_steps."""
+    import torch
+    stages = (("pre_ln", lambda: blk.pre_ln()),
+              ("attn", lambda: [blk.attn(r) for r in range(cfg.world)]),
+              ("reduce1", lambda: blk.reduce1()),
+              ("mlp_col", lambda: [blk.mlp_col(r) for r in range(cfg.world)]),
+              ("mlp_row", lambda: [blk.mlp_row(r) for r in range(cfg.world)]),
+              ("reduce2", lambda: blk.reduce2()))
+    ev = {k: [] for k, _ in stages}
+    for _ in range(n_steps):
+        for key, fn in stages:
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[key].append((a, b))
+    torch.cuda.synchronize()
+    return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) / LAUNCHES[k]
+            for k, v in ev.items()}
+
+
+def oracle_full(cfg, t) -> dict:
+    """The float64 oracle of a whole workload (every rank, and the reduce), timed on this
+    host's cores.  Its matrix products are numpy's float64 BLAS (threaded over the host's
+    cores); everything else is elementwise numpy."""
+    import oracle.tp_oracle as O
+    P = cfg.world
+    t0 = time.perf_counter()
+    if cfg.kind == "mlp":
+        X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
+        parts = [O.mlp_shard(X, A, B, r, P) for r in range(P)]
+        if cfg.dtype == "bf16":
+            O.reduce_residual_layernorm(parts, X, t["gamma"].values(), t["beta"].values(), cfg.eps)
+        else:
+            O.reduce_partials(parts)
+    elif cfg.kind == "linear":
+        X, W = t["X"].values(), t["W"].values()
+        O.col_linear(X, W, 0, P)
+        O.reduce_partials([O.row_linear_partial(X, W, r, P) for r in range(P)])
+    else:
+        X = t["X"].values()
+        qkv = np.hstack([t["Wq"].values(), t["Wk"].values(), t["Wv"].values()])
+        Wo = t["Wo"].values()
+        O.reduce_partials([O.attn_head_shard(X, qkv, Wo, cfg.n_heads, cfg.head_dim, r, P,
+                                             cfg.batch, cfg.seq, cfg.causal) for r in range(P)])
+    return {"seconds": time.perf_counter() - t0}
+
+
+def other_workloads_leg(dev, steps: int = 5, flush=None, cpu: bool = True) -> dict:
     """The other workloads of this path, each on its own and outside `value`: the fp32 MLP
     (2 ranks, 64 tokens), the single linear (rank 0's column block and both row partials),
     the bf16 MLP shard (4 ranks, 4096 tokens) and the attention-head shard (4 ranks, 16 heads
     each).  Each stage runs for every rank back to back, with HIP events only at the stage
     boundaries; 1 untimed step, then `steps` timed ones.  Per-rank times are a stage's
-    interval over its rank count."""
+    interval over its rank count.  With `flush`, a second pass times each stage again with
+    the scratch written just before it (the `cold_` figures; the others are warm: each stage
+    follows the previous one).  With `cpu`, the float64 oracle of the whole workload is timed
+    on this host (`cpu_oracle`)."""
     import torch
     from megatron_tensor_transformer_linear_amd import pipeline as pl
 
     stream = torch.cuda.current_stream()
 
-    def run(stages, n_steps):
+    def run(stages, n_steps, cold=False):
         ev = {k: [] for k, _ in stages}
         for it in range(n_steps + 1):
             prev = torch.cuda.Event(enable_timing=True)
             prev.record(stream)
             for key, fn in stages:
+                if cold:
+                    flush()
+                    prev = torch.cuda.Event(enable_timing=True)
+                    prev.record(stream)
                 fn()
                 e = torch.cuda.Event(enable_timing=True)
                 e.record(stream)
@@ -289,6 +466,10 @@ def other_workloads_leg(dev, steps: int = 5) -> dict:
                 prev = e
         torch.cuda.synchronize()
         return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+
+    def timed(stages):
+        """(warm, cold) stage milliseconds; cold is None without a flush."""
+        return run(stages, steps), (run(stages, steps, cold=True) if flush else None)
 
     out = {}
     for name in ("mlp_f32_tp2", "linear_bf16_tp2", "mlp_bf16_tp4", "attn_bf16_tp4"):
@@ -302,9 +483,9 @@ def other_workloads_leg(dev, steps: int = 5) -> dict:
             sh = pl.MLPShard(up(t["X"]), up(t["A"]), up(t["B"]), P, cfg.dtype,
                              gamma=up(t["gamma"]), beta=up(t["beta"]), eps=cfg.eps,
                              residual_ln=cfg.dtype == "bf16")
-            ms = run((("column", lambda: [sh.column(r) for r in range(P)]),
-                      ("row", lambda: [sh.row(r) for r in range(P)]),
-                      ("reduce", sh.reduce)), steps)
+            ms, cms = timed((("column", lambda: [sh.column(r) for r in range(P)]),
+                             ("row", lambda: [sh.row(r) for r in range(P)]),
+                             ("reduce", sh.reduce)))
             shard_ms = (ms["column"] + ms["row"]) / P
             rb = reduce_bytes(T, H, P, cfg.dtype, residual=sh.residual_ln, h_out=True,
                               y_out=sh.residual_ln) if cfg.dtype == "bf16" else \
@@ -315,26 +496,42 @@ def other_workloads_leg(dev, steps: int = 5) -> dict:
                      "tflops_per_rank": round((fl["mlp_col"] + fl["mlp_row"]) / shard_ms / 1e9, 1),
                      "reduce_us": round(ms["reduce"] * 1e3, 2),
                      "reduce_gbs": round(rb / ms["reduce"] / 1e6, 1)}
+            if cms:
+                entry.update({"cold_column_us": round(cms["column"] / P * 1e3, 2),
+                              "cold_row_us": round(cms["row"] / P * 1e3, 2),
+                              "cold_reduce_us": round(cms["reduce"] * 1e3, 2),
+                              "cold_reduce_gbs": round(rb / cms["reduce"] / 1e6, 1),
+                              "cold_reduce_hbm_frac": round(rb / cms["reduce"] / 1e6 /
+                                                            PEAK_HBM_GBS, 3)})
+            entry["reduce_hbm_frac"] = round(rb / ms["reduce"] / 1e6 / PEAK_HBM_GBS, 3)
         elif cfg.kind == "linear":
             sh = pl.LinearShard(up(t["X"]), up(t["W"]), P, cfg.dtype, col_ranks=(0,))
-            ms = run((("column", lambda: sh.column(0)),
-                      ("row", lambda: [sh.row(r) for r in range(P)]),
-                      ("reduce", sh.reduce)), steps)
+            ms, cms = timed((("column", lambda: sh.column(0)),
+                             ("row", lambda: [sh.row(r) for r in range(P)]),
+                             ("reduce", sh.reduce)))
             rb = reduce_bytes(T, cfg.n_out, P, "f32", residual=False, h_out=True, y_out=False)
             entry = {"column_rank0_us": round(ms["column"] * 1e3, 2),
                      "column_tflops": round(fl["col"] / ms["column"] / 1e9, 1),
                      "row_us_per_rank": round(ms["row"] / P * 1e3, 2),
                      "row_tflops": round(fl["row"] / (ms["row"] / P) / 1e9, 1),
                      "reduce_us": round(ms["reduce"] * 1e3, 2),
-                     "reduce_gbs": round(rb / ms["reduce"] / 1e6, 1)}
+                     "reduce_gbs": round(rb / ms["reduce"] / 1e6, 1),
+                     "reduce_hbm_frac": round(rb / ms["reduce"] / 1e6 / PEAK_HBM_GBS, 3)}
+            if cms:
+                entry.update({"cold_column_rank0_us": round(cms["column"] * 1e3, 2),
+                              "cold_row_us_per_rank": round(cms["row"] / P * 1e3, 2),
+                              "cold_reduce_us": round(cms["reduce"] * 1e3, 2),
+                              "cold_reduce_gbs": round(rb / cms["reduce"] / 1e6, 1),
+                              "cold_reduce_hbm_frac": round(rb / cms["reduce"] / 1e6 /
+                                                            PEAK_HBM_GBS, 3)})
             shard_ms = ms["column"]
             entry["tflops_per_rank"] = entry["column_tflops"]
         else:
             qkv = np.ascontiguousarray(np.hstack([t["Wq"].data, t["Wk"].data, t["Wv"].data]))
             sh = pl.AttnShard(up(t["X"]), pl.to_device(qkv, "bf16", dev), up(t["Wo"]), P,
                               cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, cfg.causal)
-            ms = run((("shard", lambda: [sh.rank(r) for r in range(P)]),
-                      ("reduce", sh.reduce)), steps)
+            ms, cms = timed((("shard", lambda: [sh.rank(r) for r in range(P)]),
+                             ("reduce", sh.reduce)))
             shard_ms = ms["shard"] / P
             rb = reduce_bytes(T, H, P, "f32", residual=False, h_out=True, y_out=False)
             entry = {"shard_us_per_rank": round(shard_ms * 1e3, 2),
@@ -342,7 +539,23 @@ def other_workloads_leg(dev, steps: int = 5) -> dict:
                                               shard_ms / 1e9, 1),
                      "sum_of_partials_us": round(ms["reduce"] * 1e3, 2),
                      "sum_of_partials_gbs": round(rb / ms["reduce"] / 1e6, 1)}
+            if cms:
+                entry.update({"cold_shard_us_per_rank": round(cms["shard"] / P * 1e3, 2),
+                              "cold_sum_of_partials_us": round(cms["reduce"] * 1e3, 2),
+                              "cold_sum_of_partials_gbs": round(rb / cms["reduce"] / 1e6, 1)})
         entry["pct_of_peak"] = round(100 * entry["tflops_per_rank"] / peak, 2)
+        if cpu:
+            gpu_ms = sum(ms.values())  # every rank and the reduce, warm
+            flops = P * sum(fl.values()) if cfg.kind != "linear" else fl["col"] + P * fl["row"]
+            o = oracle_full(cfg, t)
+            entry["cpu_oracle"] = {
+                "kind": "oracle", "cores": len(os.sched_getaffinity(0)),
+                "seconds": round(o["seconds"], 3),
+                "value": round(flops / o["seconds"] / 1e12, 4), "unit": "TFLOP/s",
+                "sample": (f"the whole workload, every rank and the reduce ({flops / 1e9:.1f} "
+                           "GFLOP), float64; its matrix products are numpy float64 BLAS"),
+                "gpu_ms_same_work": round(gpu_ms, 4),
+                "gpu_speedup": round(o["seconds"] * 1e3 / gpu_ms, 1)}
         out[name] = entry
         del sh, t
         torch.cuda.empty_cache()
@@ -363,6 +576,10 @@ def main() -> int:
                          "bf16 MLP shard, attention-head shard)")
     ap.add_argument("--no-fold", action="store_true",
                     help="skip the measurement of the step with folded reduces")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache pass (each stage after a 512 MiB scratch write)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the GPU clocks through amdsmi during the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain copy kernel over MIB mebibytes (reads and writes "
                          "MIB each), the known-size reference for HBM byte counters")
@@ -414,13 +631,19 @@ def main() -> int:
         step(False)
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
+    clocks = None if args.no_clock else ClockSampler()
     torch.cuda.synchronize()
+    if clocks:
+        clocks.start()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    clock = clocks.stop() if clocks else None
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
+    sclk = (clock or {}).get("sclk_mhz") or {}
+    sclk_ghz = sclk.get("mean", 0) / 1e3 if sclk else None
 
     def avg_ms(key):  # per launch: the stage's event interval over its launches
         return float(np.mean([s.elapsed_time(e) for s, e in ev[key]])) / LAUNCHES[key]
@@ -430,9 +653,6 @@ def main() -> int:
     value = step_flops * args.steps / elapsed / 1e12
     ms_step = elapsed / args.steps * 1e3
 
-    col_ms = avg_ms("mlp_col")
-    col_flops = fl["mlp_col"]
-    achieved = col_flops / (col_ms * 1e-3) / 1e12
     T, H = cfg.tokens, cfg.hidden
     r1_bytes = reduce_bytes(T, H, cfg.world, "bf16", residual=True, h_out=True, y_out=True)
     r2_bytes = reduce_bytes(T, H, cfg.world, "bf16", residual=True, h_out=True, y_out=False)
@@ -450,6 +670,40 @@ def main() -> int:
             entry["gbs"] = round(nbytes / ms / 1e6, 1)
             entry["hbm_frac"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)
         stages[key] = entry
+    if not args.no_cold:
+        log("cold-cache pass over the stages")
+        cold = cold_stages(cfg, blk, stream, CacheFlush(dev), max(2, min(args.steps, 5)))
+        for key, ms in cold.items():
+            e = stages[key]
+            e["cold_avg_ms"] = round(ms, 4)
+            if "tflops" in e:
+                fl_key = (fl["qkv"] + fl["attn_core"] + fl["o_proj"]) if key == "attn" else fl[key]
+                e["cold_tflops"] = round(fl_key / ms / 1e9, 1)
+            if "gbs" in e:
+                nbytes = {"reduce1": r1_bytes, "reduce2": r2_bytes, "pre_ln": ln_bytes}[key]
+                e["cold_gbs"] = round(nbytes / ms / 1e6, 1)
+                e["cold_hbm_frac"] = round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)
+
+    # Roofline of the MLP's two GEMMs, each one launch shape (8192 x 12288 x 6144 and
+    # 8192 x 6144 x 12288, 1236.95 GFLOP): flops per launch over the launch's average duration
+    # from the timed steps' events.  `roofline` is the one with more time per step.
+    kernels = {"mlp_col": "gemm_bf16_kernel<256,256,EPI_GELU_TANH,LAY_NN> (MLP column GEMM + "
+                          "GeLU, 8192x12288x6144, bf16 out)",
+               "mlp_row": "gemm_bf16_kernel<256,256,EPI_PARTIAL_F32,LAY_NN> (MLP row GEMM, "
+                          "8192x6144x12288, fp32 partial)"}
+    rooflines = {}
+    for key, name in kernels.items():
+        ms = avg_ms(key)
+        achieved = fl[key] / (ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 1),
+             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(key),
+             "flops_per_launch": fl[key], "avg_launch_ms": round(ms, 4),
+             "time_per_step_ms": round(ms * LAUNCHES[key], 4)}
+        if sclk_ghz:
+            r["frac_at_measured_sclk"] = round(achieved / (PEAK_BF16_TFLOPS * sclk_ghz / 2.4), 4)
+        rooflines[key] = r
+    dominant = max(rooflines, key=lambda k: rooflines[k]["time_per_step_ms"])
 
     result = {
         "metric": "TFLOP/s per TP-rank layer shard (MLP+attn) and % of MI355X bf16 MFMA peak",
@@ -473,24 +727,19 @@ def main() -> int:
             "step_gflop": round(step_flops / 1e9, 1),
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },
-        "roofline": {
-            "bound": "mfma",
-            "kernel": "gemm_bf16_kernel<EPI_GELU_TANH> (MLP column GEMM + GeLU, 8192x12288x6144)",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(),
-            "flops_per_launch": col_flops,
-            "avg_launch_ms": round(col_ms, 4),
-        },
+        "roofline": rooflines[dominant],
+        "rooflines": rooflines,
+        "clock": clock,
         "stages": stages,
         # One simulated rank's layer shard (its attention-head shard and its MLP shard), the
         # unit the metric names: the rank's algorithmic flops over the sum of its stages'
         # per-launch times (the reduces and the pre-LayerNorm are the all-reduce replacement
         # and are left out here; `value` includes them).
-        "rank_shard": rank_shard(fl, stages),
+        "rank_shard": rank_shard(fl, stages, sclk_ghz),
     }
+    if sclk_ghz:
+        result["config"]["pct_of_bf16_peak_at_measured_sclk"] = round(
+            100 * value / (PEAK_BF16_TFLOPS * sclk_ghz / 2.4), 2)
     # Sequence-parallel epilogue (outside the timed step): rank r's reduce-scatter of the 8
     # partials over its 1024 rows, fused with the residual add and LayerNorm, into its rows of
     # the full buffers (the all-gather).  Same kernel as reduce1, on a row range.
@@ -518,7 +767,8 @@ def main() -> int:
         result["mlp_backward"] = mlp_backward_leg(cfg, t, blk, stream)
     if not args.no_workloads:
         log("timing the other workloads")
-        result["other_workloads"] = other_workloads_leg(dev)
+        result["other_workloads"] = other_workloads_leg(
+            dev, flush=None if args.no_cold else CacheFlush(dev), cpu=not args.no_cpu_baseline)
     if not args.no_fold:
         log("timing the block step with folded reduces")
         result["folded_step"] = folded_block_leg(cfg, blk, stream, max(1, min(args.steps, 5)))

@@ -2,21 +2,25 @@
 // dispatch over operand layouts.  The kernel itself is in gemm_bf16_kernel.hpp; the LAY_NT
 // and LAY_TN kernels of the backward products are built in gemm_bf16_nt.hip and
 // gemm_bf16_tn.hip.
+#include <atomic>
+
 #include "gemm_bf16_kernel.hpp"
 
 namespace tpk {
 
+// The count is cached per device in atomics: concurrent first calls on one device may both
+// query it, and both store the same value.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 hipError_t launch_shape_nn(int bm, int bn, const GemmDesc& g, hipStream_t stream) {

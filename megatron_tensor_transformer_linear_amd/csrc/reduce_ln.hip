@@ -254,10 +254,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
 // one row per workgroup, which measured faster for it.
 template <int THREADS, int NCH>
 hipError_t launch_t(const ReduceDesc& r, hipStream_t stream) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cus();
   const int64_t blocks = r.n_parts > 0 ? min(r.rows, (int64_t)16 * cus) : r.rows;
   dim3 grid((unsigned)blocks), block(THREADS);
   const bool full = r.H == (int64_t)NCH * THREADS * 8;

@@ -32,8 +32,10 @@ def test_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     for f in kv["kernel_sources"].split():
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if h.hexdigest() == kv["kernel_sources_sha256"].strip():
-        assert isinstance(bench.measured_traffic(), int)
+        for role in ("mlp_col", "mlp_row"):
+            assert isinstance(bench.measured_traffic(role), int)
+    assert bench.measured_traffic("no_such_role") is None
     stale = tmp_path / "traffic.md"
     stale.write_text(src.replace(kv["kernel_sources_sha256"].strip(), "0" * 64))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic("mlp_row") is None

@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import oracle.tp_oracle as O
-from gpu_helpers import check, check_exact, dev, dev_values, host, sample_rows, say
+from gpu_helpers import (block_rows, check, check_exact, dev, dev_values, host, sample_rows,
+                         say)
 from workloads import generate, get_config
 from workloads.configs import small_variant
 from workloads.synth import from_values, integer_matrix, random_affine
@@ -381,6 +382,26 @@ def test_row_edge_shapes(lib, dtype, T, K, N, world, rank):
     check("row partial", Z, O.row_linear_partial(Xv[:, :K], Wv, rank, world), dtype)
 
 
+def test_f32_column_many_row_tiles(lib):
+    """An fp32 column call with more row tiles (65600 of 64 rows) than one grid dimension
+    holds: every tile is computed (sampled rows, including the last tile, against the
+    oracle)."""
+    tp, pl = lib
+    T, H, N = 64 * 65600 - 24, 8, 16
+    rng = np.random.Generator(np.random.PCG64(65600))
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((H, N)) / np.sqrt(H)).astype(np.float32)
+    Xd, Wd = dev_values(X, "f32"), dev_values(W, "f32")
+    Y = torch.full((T, N // 2), float("nan"), dtype=torch.float32, device=Xd.device)
+    say(f"  fp32 column with many row tiles T={T} H={H} N={N}")
+    tp.tp_col_linear_gelu(Xd, Wd, Y, N // 2, T, H, N, 1, 2, tp.TP_ACT_GELU_TANH, tp.TP_F32)
+    _sync()
+    assert bool(torch.isfinite(Y).all())
+    rows = np.unique(np.concatenate([np.arange(0, T, 4093), np.arange(T - 70, T)]))
+    check("column (rows)", Y[rows], O.col_linear(X.astype(np.float64), W.astype(np.float64),
+                                                 1, 2, "gelu_tanh", rows), "f32")
+
+
 @pytest.mark.parametrize("T,H,nl,tile", [
     (8190, 136, 1016, "256x128"),  # 32 x 8 tiles of 256 x 128, ragged rows and columns
     (8190, 136, 1528, "256x192"),  # 32 x 8 tiles of 256 x 192
@@ -623,13 +644,13 @@ def test_full_linear_bf16(lib):
     say(f"  full bf16 linear {cfg.name}")
     sh.step()
     _sync()
-    rows = sample_rows(cfg.tokens, 0, 1)
+    # every element: 0.2 TFLOP of float64 oracle
     X, W = t["X"].values(), t["W"].values()
-    check("column rank 0 (rows)", sh.Ycol[0][rows], O.col_linear(X, W, 0, 2, rows=rows), "bf16")
-    parts = [O.row_linear_partial(X, W, r, 2, rows=rows) for r in range(2)]
+    check("column rank 0", sh.Ycol[0], O.col_linear(X, W, 0, 2), "bf16")
+    parts = [O.row_linear_partial(X, W, r, 2) for r in range(2)]
     for r in range(2):
-        check(f"row partial {r} (rows)", sh.parts[r][rows], parts[r], "bf16")
-    check("Z (rows)", sh.Z[rows], O.reduce_partials(parts), "bf16")
+        check(f"row partial {r}", sh.parts[r], parts[r], "bf16")
+    check("Z", sh.Z, O.reduce_partials(parts), "bf16")
 
 
 @FULL
@@ -642,18 +663,19 @@ def test_full_mlp_bf16(lib):
     say(f"  full bf16 MLP {cfg.name}")
     sh.step()
     _sync()
-    rows = sample_rows(cfg.tokens, cfg.seq, 2)
+    # every element: 1.1 TFLOP of float64 oracle for the 4 ranks
     X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
-    Y = O.concat_columns([O.col_linear(X, A, r, cfg.world, "gelu_tanh", rows)
+    Y = O.concat_columns([O.col_linear(X, A, r, cfg.world, "gelu_tanh")
                           for r in range(cfg.world)])
-    check("hidden (rows)", sh.Yfull[rows], Y, "bf16")
-    parts = [O.mlp_shard(X, A, B, r, cfg.world, rows=rows) for r in range(cfg.world)]
+    check("hidden", sh.Yfull, Y, "bf16")
+    parts = [O.row_linear_partial(Y, B, r, cfg.world) for r in range(cfg.world)]
+    del Y
     for r in range(cfg.world):
-        check(f"partial rank {r} (rows)", sh.parts[r][rows], parts[r], "bf16")
-    h, y = O.reduce_residual_layernorm(parts, X[rows], t["gamma"].values(), t["beta"].values(),
+        check(f"partial rank {r}", sh.parts[r], parts[r], "bf16")
+    h, y = O.reduce_residual_layernorm(parts, X, t["gamma"].values(), t["beta"].values(),
                                        cfg.eps)
-    check("h (rows)", sh.h[rows], h, "bf16")
-    check("y (rows)", sh.y[rows], y, "bf16")
+    check("h", sh.h, h, "bf16")
+    check("y", sh.y, y, "bf16")
 
 
 @FULL
@@ -667,7 +689,7 @@ def test_full_attention(lib):
     say(f"  full attention {cfg.name}")
     sh.step()
     _sync()
-    rows = sample_rows(cfg.tokens, cfg.seq, 3)
+    rows = block_rows(cfg.tokens, cfg.seq, 3)
     _, A = sh.workspace_views()
     r_last = cfg.world - 1
     check(f"heads rank {r_last} (rows)", A[rows],
@@ -691,7 +713,7 @@ def test_full_block(lib):
     sh.attention_phase()
     _sync()
     T, S = cfg.tokens, cfg.seq
-    rows = np.array([0, 1, 127, 128, 1000, 2047, 3 * S + 5, 3 * S + 1500, 4 * S - 1])
+    rows = block_rows(T, S, 7)  # every 128-row block, every sequence's first and last row
     attn_parts = [host(sh.parts[r][rows]) for r in range(cfg.world)]
     xn = host(sh.xn[rows])
     say("  full block: attention phase done, running reduce + MLP")
