@@ -18,7 +18,10 @@
  *   - A linear layer is Y = X.W with X [seq, H] and W [H, N] (pwwt.cn section 1.1); every
  *     matrix is row-major.  Weights are stored [in, out].
  *   - All tensor pointers are DEVICE pointers, allocated and owned by the caller.  The
- *     library allocates nothing, frees nothing and keeps no pointer after returning.
+ *     library allocates nothing, frees nothing and keeps no pointer after returning.  Its one
+ *     piece of device memory is the static scratch array of tp_attn_head_shard_noalloc
+ *     (TP_ATTN_SCRATCH_BYTES per GPU, held from when the library's device code is loaded on
+ *     that GPU until the process ends).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every call is
  *     asynchronous on that stream and never synchronises.
  *   - Ranks are numbered 0..world-1; rank r owns block r of a split dimension, and rank 0
@@ -55,7 +58,8 @@ typedef enum {
   TP_ERR_DTYPE = -5,     /* unknown dtype / activation, or a dtype the call does not support */
   TP_ERR_ALIGN = -6,     /* pointer, leading dimension or shard offset misaligned */
   TP_ERR_WORKSPACE = -7, /* workspace NULL or smaller than tp_attn_workspace_bytes */
-  TP_ERR_LAUNCH = -8     /* the HIP runtime reported an error at launch */
+  TP_ERR_LAUNCH = -8,    /* the HIP runtime reported an error at launch */
+  TP_ERR_SCRATCH = -9    /* the sizes need more than the library's static scratch */
 } tp_status;
 
 typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;         /* io dtype of X, W, Y, residual, LN */
@@ -225,6 +229,34 @@ int tp_attn_head_shard_fold(const void* Xn, const void* Wqkv, const void* Wo, fl
                             int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
                             int rank, int world, int causal, int accumulate, int dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the library's own scratch array (one per GPU) that tp_attn_head_shard_noalloc uses
+ * as its workspace: 160 MiB, what tp_attn_workspace_bytes gives for one rank of the largest
+ * workload served (8192 tokens, 12 heads of 128 per rank, H = 12288, on 256 compute units:
+ * QKV_r 75.5 MB + A_r 25.2 MB + the split strip's fp32 partials 67.1 MB). */
+#define TP_ATTN_SCRATCH_BYTES ((size_t)160 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): tp_attn_head_shard without the workspace argument.
+ * The workspace is taken from a static device array of TP_ATTN_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the call itself allocates nothing
+ * (no hipMalloc or hipFree, no allocating library routine).  Its first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress), which loads the library's device
+ * code there if it is not loaded yet: make one call on each device before capturing a graph.
+ * Arguments, results and errors are those of tp_attn_head_shard, with the outputs
+ * bit-identical to it for the same inputs, except:
+ *   - sizes whose tp_attn_workspace_bytes exceeds TP_ATTN_SCRATCH_BYTES return TP_ERR_SCRATCH
+ *     (before any launch);
+ *   - every call on one GPU shares that GPU's array, which keeps the last call's QKV_r and
+ *     A_r: calls that overlap in time on one GPU (on different streams, or from different
+ *     threads without ordering) race and give undefined results.  Order them on one stream.
+ *     No part of the array needs clearing: every byte a call reads it wrote first.
+ * Errors: TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DIVISIBLE, TP_ERR_RANK, TP_ERR_DTYPE,
+ * TP_ERR_ALIGN, TP_ERR_SCRATCH, TP_ERR_LAUNCH (also when the array's address cannot be
+ * obtained on the current device). */
+int tp_attn_head_shard_noalloc(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
+                               int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                               int rank, int world, int causal, int dtype, void* stream);
 
 /* The all-reduce replacement, fused with the residual add and LayerNorm (pwwt.cn section
  * 2.3: the single all-reduce sits just before the residual add, and fusing it with the

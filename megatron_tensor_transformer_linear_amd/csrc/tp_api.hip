@@ -4,10 +4,19 @@
 // call launches nothing and leaves its outputs untouched.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/tp_shard.h"
 #include "common.hpp"
 
 using namespace tpk;
+
+// The library's own scratch for tp_attn_head_shard_noalloc, the entry point for callers that
+// cannot allocate: one array per GPU, held from the module's load until the process ends.
+// Host code never passes the array's name to a kernel or a copy (on the host it names a
+// stand-in, not device memory); it uses the device address hipGetSymbolAddress returns for
+// the current device (scratch_address below).
+static __device__ __align__(256) char scratch[TP_ATTN_SCRATCH_BYTES];
 
 namespace {
 
@@ -155,6 +164,28 @@ int attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpa
   return launched(launch_gemm_bf16(o, st));
 }
 
+// Device address of `scratch` on the current device, looked up once per device (each GPU
+// holds its own copy of the array at its own address).
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return TP_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return TP_ERR_LAUNCH;
+    }
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,6 +201,9 @@ const char* tp_status_string(int status) {
     case TP_ERR_ALIGN: return "TP_ERR_ALIGN: misaligned pointer, leading dimension or shard offset";
     case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
     case TP_ERR_LAUNCH: return "TP_ERR_LAUNCH: kernel launch failed";
+    case TP_ERR_SCRATCH:
+      return "TP_ERR_SCRATCH: the sizes need more than the library's static scratch "
+             "(TP_ATTN_SCRATCH_BYTES per GPU)";
     default: return "unknown tp_status";
   }
 }
@@ -408,6 +442,25 @@ int tp_attn_head_shard_fold(const void* Xn, const void* Wqkv, const void* Wo, fl
   return attn_head_shard(Xn, Wqkv, Wo, Zsum, batch, seq, H, n_heads, head_dim, rank, world,
                          causal, accumulate ? EPI_ACC_F32 : EPI_PARTIAL_F32, dtype, workspace,
                          workspace_bytes, stream);
+}
+
+int tp_attn_head_shard_noalloc(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
+                               int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                               int rank, int world, int causal, int dtype, void* stream) {
+  // Every check of tp_attn_head_shard except the workspace's, then the size limit, all before
+  // the scratch lookup (the first call on a device) and any launch.
+  if (!Xn || !Wqkv || !Wo || !Zpart) return TP_ERR_NULL;
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;
+  if (int st = check_rank(rank, world)) return st;
+  AttnSizes s;
+  if (int st = attn_sizes(batch, seq, H, n_heads, head_dim, world, &s)) return st;
+  if ((uint64_t)s.total > (uint64_t)TP_ATTN_SCRATCH_BYTES) return TP_ERR_SCRATCH;
+  if (!aligned16(Xn) || !aligned16(Wqkv) || !aligned16(Wo) || !aligned16(Zpart))
+    return TP_ERR_ALIGN;
+  void* ws = nullptr;
+  if (int st = scratch_address(&ws)) return st;
+  return attn_head_shard(Xn, Wqkv, Wo, Zpart, batch, seq, H, n_heads, head_dim, rank, world,
+                         causal, EPI_PARTIAL_F32, dtype, ws, (size_t)TP_ATTN_SCRATCH_BYTES, stream);
 }
 
 int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_stride,

@@ -22,6 +22,8 @@ TP_ERR_DTYPE = -5
 TP_ERR_ALIGN = -6
 TP_ERR_WORKSPACE = -7
 TP_ERR_LAUNCH = -8
+TP_ERR_SCRATCH = -9
+TP_ATTN_SCRATCH_BYTES = 160 << 20
 
 TP_F32 = 0
 TP_BF16 = 1
@@ -31,7 +33,7 @@ TP_ACT_GELU_TANH = 1
 EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_row_linear_fold",
             "tp_col_linear_gelu_save", "tp_row_linear_backward", "tp_col_linear_backward",
             "tp_attn_workspace_bytes", "tp_attn_head_shard", "tp_attn_head_shard_fold",
-            "tp_partial_reduce_residual_ln",
+            "tp_attn_head_shard_noalloc", "tp_partial_reduce_residual_ln",
             "tp_partial_reduce_scatter_residual_ln", "tp_status_string")
 
 if not os.path.exists(LIB_PATH):
@@ -65,6 +67,9 @@ lib.tp_attn_head_shard.restype = _int
 lib.tp_attn_head_shard_fold.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
                                         _int, _int, _int, _int, _vp, _sz, _vp]
 lib.tp_attn_head_shard_fold.restype = _int
+lib.tp_attn_head_shard_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
+                                           _int, _int, _int, _vp]
+lib.tp_attn_head_shard_noalloc.restype = _int
 lib.tp_partial_reduce_residual_ln.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp, _vp,
                                               _i64, _i64, _int, _vp]
 lib.tp_partial_reduce_residual_ln.restype = _int
@@ -174,6 +179,15 @@ def tp_attn_head_shard_fold(Xn, Wqkv, Wo, Zsum, batch: int, seq: int, H: int, n_
                                               int(accumulate), dtype, _ptr(workspace),
                                               workspace_bytes, _stream(stream)),
                   "tp_attn_head_shard_fold")
+
+
+def tp_attn_head_shard_noalloc(Xn, Wqkv, Wo, Zpart, batch: int, seq: int, H: int, n_heads: int,
+                               head_dim: int, rank: int, world: int, causal: int, dtype: int,
+                               stream=None) -> int:
+    return _check(lib.tp_attn_head_shard_noalloc(_ptr(Xn), _ptr(Wqkv), _ptr(Wo), _ptr(Zpart),
+                                                 batch, seq, H, n_heads, head_dim, rank, world,
+                                                 int(causal), dtype, _stream(stream)),
+                  "tp_attn_head_shard_noalloc")
 
 
 def tp_partial_reduce_residual_ln(parts, n_parts: int, part_stride: int, residual, gamma, beta,

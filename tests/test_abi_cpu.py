@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol(tp):
 
 
 def test_status_strings(tp):
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = tp.tp_status_string(code)
         assert s.startswith("TP_OK" if code == 0 else "TP_ERR_")
     assert tp.tp_status_string(-100) == "unknown tp_status"
@@ -85,6 +85,15 @@ def attn(tp, **kw):
     return tp.lib.tp_attn_head_shard(a["Xn"], a["Wqkv"], a["Wo"], a["Z"], a["batch"], a["seq"],
                                      a["H"], a["nh"], a["d"], a["rank"], a["world"], a["causal"],
                                      a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+def attnn(tp, **kw):
+    a = dict(Xn=P, Wqkv=P, Wo=P, Z=P, batch=2, seq=64, H=1024, nh=8, d=128, rank=0, world=4,
+             causal=1, dtype=tp.TP_BF16, stream=None)
+    a.update(kw)
+    return tp.lib.tp_attn_head_shard_noalloc(a["Xn"], a["Wqkv"], a["Wo"], a["Z"], a["batch"],
+                                             a["seq"], a["H"], a["nh"], a["d"], a["rank"],
+                                             a["world"], a["causal"], a["dtype"], a["stream"])
 
 
 def rowf(tp, **kw):
@@ -223,6 +232,17 @@ CASES = [
     ("attn fold heads % world", attnf, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
     ("attn fold small workspace", attnf, dict(wsb=1000), "TP_ERR_WORKSPACE"),
     ("attn fold misaligned Z", attnf, dict(Z=P + 8), "TP_ERR_ALIGN"),
+    # attention-head shard on the library's static scratch (no workspace argument)
+    ("attn noalloc null Xn", attnn, dict(Xn=None), "TP_ERR_NULL"),
+    ("attn noalloc null Z", attnn, dict(Z=None), "TP_ERR_NULL"),
+    ("attn noalloc f32", attnn, dict(dtype=0), "TP_ERR_DTYPE"),
+    ("attn noalloc bad rank", attnn, dict(rank=-1), "TP_ERR_RANK"),
+    ("attn noalloc H != heads*d", attnn, dict(H=1000), "TP_ERR_SHAPE"),
+    ("attn noalloc heads % world", attnn, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("attn noalloc misaligned Wqkv", attnn, dict(Wqkv=P + 8), "TP_ERR_ALIGN"),
+    # 8 x 4096 tokens, 12 heads per rank: QKV_r alone is 302 MB, beyond the 160 MiB scratch
+    ("attn noalloc beyond the scratch", attnn,
+     dict(batch=8, seq=4096, H=12288, nh=96, world=8), "TP_ERR_SCRATCH"),
     # reduce + residual + LN
     ("reduce bad dtype", red, dict(dtype=9), "TP_ERR_DTYPE"),
     ("reduce negative parts", red, dict(n=-1), "TP_ERR_SHAPE"),
@@ -319,6 +339,23 @@ def test_workspace_bytes_split_strip(tp):
     T, nb = 4 * 2048, (96 // 8) * 128
     plain = (T * 3 * nb * 2 + T * nb * 2 + 255) // 256 * 256
     assert tp.tp_attn_workspace_bytes(4, 2048, 12288, 96, 128, 8, tp.TP_BF16) == plain + 4 * T * 512 * 4
+
+
+def test_scratch_limit_fits_the_block_workload(tp):
+    """The static scratch holds the workspace of one rank of the largest workload (8192
+    tokens, 12 heads of 128 per rank, H = 12288) on 256 compute units, exactly; twice the
+    tokens do not fit."""
+    need = tp.tp_attn_workspace_bytes(4, 2048, 12288, 96, 128, 8, tp.TP_BF16)
+    assert need == tp.TP_ATTN_SCRATCH_BYTES
+    assert tp.tp_attn_workspace_bytes(8, 2048, 12288, 96, 128, 8, tp.TP_BF16) > \
+        tp.TP_ATTN_SCRATCH_BYTES
+    assert attnn(tp, batch=8, seq=2048, H=12288, nh=96, world=8) == tp.TP_ERR_SCRATCH
+
+
+def test_header_scratch_size_matches_binding(tp):
+    src = open(HEADER).read()
+    m = re.search(r"#define TP_ATTN_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == tp.TP_ATTN_SCRATCH_BYTES
 
 
 def test_python_wrapper_raises(tp):
