@@ -16,19 +16,19 @@ step's algorithmic flops (all 8 ranks' shards) divided by the measured step time
 TFLOP/s, over steps run back to back.  Per-kernel durations come from HIP events recorded on
 the launch stream inside the timed region; the roofline object reports the kernel with the
 most time per step (one of the two MLP GEMMs), `rooflines` both.  The graphics and memory
-clocks are sampled through amdsmi during the timed steps, and the fractions of peak are also
-given at the measured graphics clock.  A cold-cache pass then times every stage again after
-writing 512 MiB of scratch (twice the 256 MB Infinity Cache) just before it, so nothing it
-reads is cached (`stages[*].cold_*`).  The CPU baseline times the float64 oracle on a bounded
-row sample of the same workload on this host, and the full oracle of each other workload.
-After the timed steps, the sequence-parallel form of the epilogue (each rank's reduce-scatter of its 1024 rows) and the backward pass of
-the MLP pair (the four gradient products of every rank and the reduce of the input-gradient
-partials; --no-backward skips it) are timed on their own and reported beside the step,
-outside `value`, and so is the same step with each epilogue's reduce folded into the
-row-parallel products (one fp32 running sum instead of 8 stacked partials; --no-fold skips
-it).  The other workloads of the path (the fp32 MLP, the single linear, the bf16 MLP shard and
-the attention-head shard) are timed the same way and reported per rank under
-`other_workloads` (--no-workloads skips them).
+clocks are sampled through amdsmi over a separate ~6 s run of the same steps, and the
+fractions of peak are also given at that graphics clock.  A cold-cache pass then times every
+stage again after writing 512 MiB of scratch (twice the 256 MB Infinity Cache) just before
+it, so nothing it reads is cached (`stages[*].cold_*`).  The CPU baseline times the float64
+oracle on a bounded row sample of the same workload on this host, and the full oracle of each
+other workload.  After the timed steps, the sequence-parallel form of the epilogue (each
+rank's reduce-scatter of its 1024 rows) and the backward pass of the MLP pair (the four
+gradient products of every rank and the reduce of the input-gradient partials; --no-backward
+skips it) are timed on their own and reported beside the step, outside `value`, and so is the
+same step with each epilogue's reduce folded into the row-parallel products (one fp32 running
+sum instead of 8 stacked partials; --no-fold skips it).  The other workloads of the path (the
+fp32 MLP, the single linear, the bf16 MLP shard and the attention-head shard) are timed the
+same way and reported per rank under `other_workloads` (--no-workloads skips them).
 """
 from __future__ import annotations
 
@@ -85,10 +85,13 @@ def measured_traffic(role: str):
 class ClockSampler:
     """Samples the GPU's graphics clock (mean over its XCDs), memory clock and socket power
     through amdsmi's GPU metrics every `period` seconds on a thread, between start() and
-    stop().  amdsmi reads the driver's metrics table; it makes no HIP call.  Any failure (no
-    amdsmi, no matching device) leaves the summary's `error` set instead of clocks."""
+    stop().  amdsmi reads the driver's metrics table; it makes no HIP call.  The firmware
+    refreshes that table far less often than every step, so only samples whose firmware
+    timestamp changed are kept, and the bench samples a run of several seconds (clock_leg).
+    Any failure (no amdsmi, no matching device) leaves the summary's `error` set instead of
+    clocks."""
 
-    def __init__(self, period: float = 0.02):
+    def __init__(self, period: float = 0.05):
         import threading
         self.period, self.samples, self.error = period, [], None
         self._stop = threading.Event()
@@ -131,15 +134,19 @@ class ClockSampler:
         if not gfx and self._num(m.get("current_gfxclk")):
             gfx = [self._num(m["current_gfxclk"])]
         return (sum(gfx) / len(gfx) if gfx else None, self._num(m.get("current_uclk")),
-                self._num(m.get("current_socket_power")))
+                self._num(m.get("current_socket_power")), m.get("firmware_timestamp"))
 
     def _run(self):
+        last = None
         while not self._stop.wait(self.period):
             try:
-                self.samples.append(self._read())
+                x = self._read()
             except Exception as e:  # noqa: BLE001
                 self.error = f"amdsmi read failed: {e}"
                 return
+            if x[3] is None or x[3] != last:  # a refreshed table (or no timestamp to tell)
+                self.samples.append(x[:3])
+                last = x[3]
 
     def start(self):
         if self._handle is None:
@@ -153,8 +160,8 @@ class ClockSampler:
             self._stop.set()
             self._thread.join()
         out = {"source": "amdsmi GPU metrics (current_gfxclks averaged over the XCDs, "
-                         f"current_uclk, current_socket_power), every {self.period * 1e3:.0f} ms "
-                         "through the timed steps",
+                         f"current_uclk, current_socket_power), polled every "
+                         f"{self.period * 1e3:.0f} ms, one sample per firmware refresh",
                "samples": len(self.samples)}
         if self.error:
             out["error"] = self.error
@@ -377,6 +384,29 @@ def stage_step(cfg, blk, stream, ev):
                 ev[key].append((prev, e))
                 prev = e
     return step
+
+
+def clock_leg(step, ms_per_step: float, seconds: float = 6.0) -> dict:
+    """The block step back to back for about `seconds` while the clocks are sampled; the
+    first second (the clock settling under load) is left out of the summary."""
+    import torch
+    n = max(1, int(seconds * 1e3 / ms_per_step))
+    sampler = ClockSampler()
+    if sampler.error:
+        return {"error": sampler.error}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step(False)
+    # sample only once the queue is full and the first second has passed
+    while time.perf_counter() - t0 < 1.0:
+        time.sleep(0.01)
+    sampler.start()
+    torch.cuda.synchronize()
+    out = sampler.stop()
+    out["steps"] = n
+    out["window_s"] = round(time.perf_counter() - t0 - 1.0, 2)
+    return out
 
 
 def cold_stages(cfg, blk, stream, flush, n_steps: int) -> dict:
@@ -631,19 +661,19 @@ def main() -> int:
         step(False)
         torch.cuda.synchronize()
         log(f"warmup step {i + 1}/{args.warmup} done")
-    clocks = None if args.no_clock else ClockSampler()
     torch.cuda.synchronize()
-    if clocks:
-        clocks.start()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    clock = clocks.stop() if clocks else None
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
+    clock = None
+    if not args.no_clock:
+        log("clock sampling over ~6 s of steps")
+        clock = clock_leg(step, elapsed / args.steps * 1e3)
     sclk = (clock or {}).get("sclk_mhz") or {}
-    sclk_ghz = sclk.get("mean", 0) / 1e3 if sclk else None
+    sclk_ghz = sclk.get("median", 0) / 1e3 if sclk else None
 
     def avg_ms(key):  # per launch: the stage's event interval over its launches
         return float(np.mean([s.elapsed_time(e) for s, e in ev[key]])) / LAUNCHES[key]

@@ -544,6 +544,8 @@ def test_attention_qkv_split_strip_integer_exact(lib):
     (3, 65, 4, 2, True),       # one key past a key block, three sequences
     (2, 130, 2, 2, False),     # one query past a query block, full attention
     (1, 257, 8, 8, True),      # one head per rank
+    (2, 300, 16, 2, True),     # 16 (sequence, head) pairs, ragged last block
+    (4, 129, 8, 4, False),     # 8 pairs, full attention, one query past a block
 ])
 def test_attention_edge_shapes(lib, batch, seq, n_heads, world, causal):
     tp, pl = lib
