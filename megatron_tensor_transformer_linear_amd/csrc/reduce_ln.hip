@@ -16,6 +16,8 @@
 // at 6.5 TB/s; the 0.4 GB of h and y it writes cost about a fifth of its time.
 // The row stays in registers: the mean is a wave shuffle reduction plus one cross-wave step
 // through LDS, and the variance is a second pass over the registers (no E[x^2] - mean^2).
+#include <atomic>
+
 #include "common.hpp"
 
 namespace tpk {
@@ -248,24 +250,185 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   }  // row loop
 }
 
+// The same operation with no partials to sum (h = residual; the pre-attention LayerNorm of
+// the block).  A workgroup loops over rows blockIdx.x, + gridDim.x, ... and issues the loads of
+// its next row before it starts on the current one, so every workgroup keeps one row's reads in
+// flight through its reductions and stores.  Three raw row buffers rotate (the loop is
+// unrolled three times), so no register copy waits on a load in flight; the row is unpacked again
+// for each of its three passes (sum, squares, output) instead of being held as fp32, and gamma
+// and beta are loaded once per workgroup into LDS.  That keeps the registers per workgroup low
+// and the rows in flight per compute unit high.  Every load of a row is issued before the previous
+// row's wait (the vector-memory counter completes in order, so a later load that the current
+// row waited on would also wait for the prefetch).  The row loads are buffer loads from a
+// resource spanning that row (none past the last row: such a resource has no bytes in range
+// and its loads return zeros), so the prefetch needs no branch.  The statistics are taken in
+// the order of reduce_ln_kernel.
+template <int THREADS, int NCH, bool BF16, bool FULL>
+__global__ __launch_bounds__(THREADS) void ln_rows_kernel(ReduceDesc r) {
+  __shared__ float red[THREADS / 64];
+  const int tid = threadIdx.x;
+  const int64_t H = r.H;
+  constexpr int ES = BF16 ? 2 : 4;
+  uint32_t boff[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) boff[c] = (uint32_t)((c * THREADS + tid) * 8 * ES);
+  auto in = [&](int c) { return FULL || (int64_t)(c * THREADS + tid) * 8 < H; };
+  const bool ln = r.gamma != nullptr, has_beta = r.beta != nullptr, has_h = r.h_out != nullptr;
+  // gamma and beta, loaded once, wait in LDS for the output pass.  Each thread reads back only
+  // the runs it wrote, so the LDS serves as per-thread storage: no barrier, and 16 consecutive
+  // bytes per lane read conflict-free.
+  __shared__ Raw8<BF16> gb[2][NCH * THREADS];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int64_t col = (int64_t)(c * THREADS + tid) * 8;
+    Raw8<BF16> g{}, b{};
+    if (ln && in(c)) {
+      g = load_raw8<BF16>(r.gamma, col);
+      if (has_beta) b = load_raw8<BF16>(r.beta, col);
+    }
+    gb[0][c * THREADS + tid] = g;
+    gb[1][c * THREADS + tid] = b;
+  }
+  auto load_row = [&](int64_t row, Raw8<BF16>(&x)[NCH]) __attribute__((always_inline)) {
+    const bool ok = row < r.rows;
+    const char* base = (const char*)r.residual + (ok ? row * H * ES : 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, ok ? (int)(H * ES) : 0, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if constexpr (BF16) {
+        x[c].u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, 0));
+      } else {
+        x[c].a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, 0));
+        x[c].b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, 0));
+      }
+    }
+  };
+  // A fresh copy of a raw run for each pass: the compiler may not keep the unpacked fp32 values
+  // of one pass for the next (that would double the row's registers).
+  auto fresh = [](Raw8<BF16> q) __attribute__((always_inline)) {
+    if constexpr (BF16) {
+      asm volatile("" : "+v"(q.u.x), "+v"(q.u.y), "+v"(q.u.z), "+v"(q.u.w));
+    } else {
+      asm volatile("" : "+v"(q.a), "+v"(q.b));
+    }
+    return q;
+  };
+  auto process = [&](int64_t row, const Raw8<BF16>(&x)[NCH]) __attribute__((always_inline)) {
+    const int64_t ooff = row * (r.ld_out > 0 ? r.ld_out : H);
+    float sum = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      float v[8];
+      unpack8<BF16>(fresh(x[c]), v);
+      if (has_h && in(c)) {
+        F8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.v[e] = v[e];
+        store8<BF16>(r.h_out, ooff + (int64_t)(c * THREADS + tid) * 8, o);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) sum += v[e] + v[e + 1];
+    }
+    if (!ln) return;
+    const float inv_h = 1.0f / (float)H;
+    const float mean = block_sum<THREADS>(sum, red) * inv_h;
+    float sq = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (in(c)) {
+        float v[8];
+        unpack8<BF16>(fresh(x[c]), v);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float a0 = v[e] - mean, a1 = v[e + 1] - mean;
+          sq += a0 * a0 + a1 * a1;
+        }
+      }
+    }
+    const float var = block_sum<THREADS>(sq, red) * inv_h;
+    const float rstd = 1.0f / sqrtf(var + r.eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (in(c)) {
+        float v[8], gv[8], bv[8];
+        unpack8<BF16>(fresh(x[c]), v);
+        unpack8<BF16>(gb[0][c * THREADS + tid], gv);
+        unpack8<BF16>(gb[1][c * THREADS + tid], bv);
+        F8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y.v[e] = (v[e] - mean) * rstd * gv[e] + bv[e];
+        store8<BF16>(r.y_out, ooff + (int64_t)(c * THREADS + tid) * 8, y);
+      }
+    }
+  };
+  // Rows are prefetched two ahead through three rotating buffers: the wait for a row's loads
+  // also covers every older access of the workgroup, and two rows back the stores have long
+  // completed, so that wait is not held up by the previous row's stores.
+  const int64_t step = gridDim.x;
+  Raw8<BF16> xa[NCH], xb[NCH], xc[NCH];
+  load_row(blockIdx.x, xa);
+  load_row(blockIdx.x + step, xb);
+  for (int64_t row = blockIdx.x; row < r.rows; row += 3 * step) {
+    load_row(row + 2 * step, xc);
+    __builtin_amdgcn_sched_barrier(0);
+    process(row, xa);
+    if (row + step >= r.rows) break;
+    load_row(row + 3 * step, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    process(row + step, xb);
+    if (row + 2 * step >= r.rows) break;
+    load_row(row + 4 * step, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    process(row + 2 * step, xc);
+  }
+}
+
+// Workgroups of one kernel instance resident per compute unit, queried once per process
+// (the first call on any device answers for all: every device here is the same gfx950).
+template <class K>
+int resident_per_cu(K kernel, int threads) {
+  static std::atomic<int> n{0};
+  int v = n.load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v <= 0) {
+      (void)hipGetLastError();
+      v = 1;
+    }
+    n.store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 // Rows per launch: a workgroup loops over rows blockIdx.x, + gridDim.x, ...  With partials
 // to sum, up to 16 workgroups per compute unit (two rows each for the 8192-row block
-// reduces: 5.72 vs 5.58 TB/s for one row per workgroup on MI355X); a plain LayerNorm keeps
-// one row per workgroup, which measured faster for it.
+// reduces: 5.72 vs 5.58 TB/s for one row per workgroup on MI355X).  Without partials, as many
+// workgroups as are resident at once, each prefetching its next rows (ln_rows_kernel, for bf16
+// rows of up to 16384 elements: its row buffers fit the registers and gamma and beta 64 KB of LDS).
+template <int THREADS, int NCH, bool BF16, bool FULL>
+hipError_t launch_variant(const ReduceDesc& r, hipStream_t stream) {
+  const int cus = device_cus();
+  if constexpr (BF16 && NCH * THREADS <= 2048) {
+    if (r.n_parts == 0) {
+      auto k = ln_rows_kernel<THREADS, NCH, BF16, FULL>;
+      const int64_t blocks = min(r.rows, (int64_t)resident_per_cu(k, THREADS) * cus);
+      hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(THREADS), 0, stream, r);
+      return hipGetLastError();
+    }
+  }
+  const int64_t blocks = min(r.rows, (int64_t)16 * cus);
+  hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, BF16, FULL>), dim3((unsigned)blocks),
+                     dim3(THREADS), 0, stream, r);
+  return hipGetLastError();
+}
+
 template <int THREADS, int NCH>
 hipError_t launch_t(const ReduceDesc& r, hipStream_t stream) {
-  const int cus = device_cus();
-  const int64_t blocks = r.n_parts > 0 ? min(r.rows, (int64_t)16 * cus) : r.rows;
-  dim3 grid((unsigned)blocks), block(THREADS);
   const bool full = r.H == (int64_t)NCH * THREADS * 8;
-  if (r.bf16) {
-    if (full) hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, true, true>), grid, block, 0, stream, r);
-    else hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, true, false>), grid, block, 0, stream, r);
-  } else {
-    if (full) hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, false, true>), grid, block, 0, stream, r);
-    else hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, false, false>), grid, block, 0, stream, r);
-  }
-  return hipGetLastError();
+  if (r.bf16) return full ? launch_variant<THREADS, NCH, true, true>(r, stream)
+                          : launch_variant<THREADS, NCH, true, false>(r, stream);
+  return full ? launch_variant<THREADS, NCH, false, true>(r, stream)
+              : launch_variant<THREADS, NCH, false, false>(r, stream);
 }
 
 }  // namespace

@@ -572,6 +572,9 @@ def test_attention_edge_shapes(lib, batch, seq, n_heads, world, causal):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("rows,H,n_parts,residual,ln", [
     (5, 8, 0, True, True),        # plain LayerNorm of a narrow row
+    (20000, 64, 0, True, True),   # LayerNorm, several rows per workgroup (odd and even counts)
+    (1000, 12288, 0, True, True), # LayerNorm at the block's width, more rows than resident groups
+    (777, 4104, 0, True, False),  # no partials, no LayerNorm: h = residual, ragged vector tail
     (300, 12288, 1, True, True),  # one partial, wide row
     (64, 4104, 3, False, True),   # no residual, ragged vector tail
     (17, 65536, 2, True, True),   # widest supported row (1024-thread path)
