@@ -204,7 +204,8 @@ size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_head
  *
  * Xn [batch*seq, H] dense: the (already normalised) input, sequences contiguous.  Wqkv
  * [H, 3H] dense = [Wq | Wk | Wv], head h owning columns [h*d, (h+1)*d) of each block.  Wo
- * [H, H] dense.  H must equal n_heads*head_dim; head_dim must be 128.  causal: key j is
+ * [H, H] dense.  H must equal n_heads*head_dim; head_dim must be 128; seq < 2^30 and
+ * batch*seq < 2^31 (TP_ERR_SHAPE otherwise).  causal: key j is
  * visible to query i iff j <= i within the same sequence.  Only dtype TP_BF16.
  * workspace (device, >= tp_attn_workspace_bytes, 256-byte aligned) receives, as a
  * documented by-product, QKV_r bf16 [T, 3*hl*d] at offset 0 and A_r bf16 [T, hl*d] right
@@ -271,7 +272,7 @@ int tp_attn_head_shard_noalloc(const void* Xn, const void* Wqkv, const void* Wo,
  * (parts may then be NULL).  residual may be NULL (treated as 0); h_out may be NULL;
  * gamma == NULL skips the LayerNorm (y_out is then ignored); beta == NULL means 0.
  * residual, gamma, beta, h_out and y_out use `dtype`; h_out and y_out must not alias the
- * parts.  Requires H % 8 == 0 and H <= 65536.
+ * parts.  Requires H % 8 == 0, H <= 65536 and 1 <= rows < 2^31.
  * Errors: TP_ERR_NULL (no input at all, or gamma given with y_out NULL), TP_ERR_SHAPE,
  * TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_LAUNCH. */
 int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_stride,

@@ -106,6 +106,13 @@ struct GemmPlan {
   int64_t n1;
 };
 GemmPlan gemm_bf16_plan(int64_t M, int64_t N, int cus);
+// Contraction ranges of the narrow strip in launch_gemm_bf16_split, and whether a plan's strip
+// is split that way (a strip of 128 x 128 tiles, K divisible into GEMM_KSPLIT ranges of whole
+// 8-element chunks).
+constexpr int GEMM_KSPLIT = 4;
+inline bool gemm_split_applies(const GemmPlan& pl, int64_t K) {
+  return pl.n1 > 0 && pl.bm1 == 128 && K % (GEMM_KSPLIT * 8) == 0;
+}
 
 hipError_t launch_gemm_bf16(const GemmDesc& g, hipStream_t stream);
 // Compute units of the current device (cached per device; 256 when it cannot be queried).

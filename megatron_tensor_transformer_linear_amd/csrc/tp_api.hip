@@ -28,6 +28,8 @@ constexpr int64_t MAX_LD_ACT = 1 << 21;
 constexpr int64_t MAX_LD_WEIGHT = 1 << 23;
 // The weight-gradient products contract over the sequence, which the tile counts in 32-bit.
 constexpr int64_t MAX_SEQ_BWD = (int64_t)1 << 30;
+// The attention kernel indexes the queries and keys of a sequence in 32 bits.
+constexpr int64_t MAX_SEQ_ATTN = ((int64_t)1 << 30) - 1;
 inline bool mult8(int64_t v) { return (v & 7) == 0; }
 
 inline int check_rank(int rank, int world) {
@@ -47,6 +49,9 @@ int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
   if (batch <= 0 || seq <= 0 || H <= 0 || n_heads <= 0 || head_dim <= 0) return TP_ERR_SHAPE;
   if ((int64_t)n_heads * head_dim != H || head_dim != 128) return TP_ERR_SHAPE;
   if (H > MAX_LD_ACT) return TP_ERR_SHAPE;
+  // the attention kernel indexes queries in 32 bits and the projections tile the tokens in
+  // 32 bits (both bounds hold before any product below is formed)
+  if (seq > MAX_SEQ_ATTN || batch > INT32_MAX || batch * seq > INT32_MAX) return TP_ERR_SHAPE;
   if (n_heads % world) return TP_ERR_DIVISIBLE;
   s->T = batch * seq;
   s->hl = n_heads / world;
@@ -473,7 +478,7 @@ int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_
   if (n_parts == 0 && !residual) return TP_ERR_NULL;
   if (gamma && !y_out) return TP_ERR_NULL;
   if (!gamma && !h_out) return TP_ERR_NULL;
-  if (rows <= 0 || H <= 0 || H > 65536) return TP_ERR_SHAPE;
+  if (rows <= 0 || rows > INT32_MAX || H <= 0 || H > 65536) return TP_ERR_SHAPE;
   if (!(eps >= 0.0f) || isinf(eps)) return TP_ERR_SHAPE;
   if (n_parts > 1 && part_stride < rows * H) return TP_ERR_SHAPE;
   if (!mult8(H)) return TP_ERR_ALIGN;
@@ -511,7 +516,7 @@ int tp_partial_reduce_scatter_residual_ln(const float* parts, int n_parts, int64
   if (n_parts == 0 && !residual) return TP_ERR_NULL;
   if (gamma && !y_out) return TP_ERR_NULL;
   if (!gamma && !h_out) return TP_ERR_NULL;
-  if (rows <= 0 || H <= 0 || H > 65536) return TP_ERR_SHAPE;
+  if (rows <= 0 || rows > INT32_MAX || H <= 0 || H > 65536) return TP_ERR_SHAPE;
   if (rows % world) return TP_ERR_DIVISIBLE;
   if (!(eps >= 0.0f) || isinf(eps)) return TP_ERR_SHAPE;
   if (n_parts > 1 && part_stride < rows * H) return TP_ERR_SHAPE;
