@@ -17,7 +17,9 @@ TFLOP/s, over steps run back to back.  Per-kernel durations come from HIP events
 the launch stream inside the timed region; the roofline object reports the kernel with the
 most time per step (one of the two MLP GEMMs), `rooflines` both.  The graphics and memory
 clocks are sampled through amdsmi over a separate ~6 s run of the same steps, and the
-fractions of peak are also given at that graphics clock.  A cold-cache pass then times every
+fractions of peak are also given at that graphics clock, and against the matrix-core rate the
+device sustains with no memory traffic at all in the same power state (`mfma_ceiling`: a
+calibration loop of MFMAs on random operands).  A cold-cache pass then times every
 stage again after writing 512 MiB of scratch (twice the 256 MB Infinity Cache) just before
 it, so nothing it reads is cached (`stages[*].cold_*`).  The CPU baseline times the float64
 oracle on a bounded row sample of the same workload on this host, and the full oracle of each
@@ -593,6 +595,53 @@ def other_workloads_leg(dev, steps: int = 5, flush=None, cpu: bool = True) -> di
     return out
 
 
+def mfma_ceiling_leg(dev, a_src, b_src, launches: int = 3, iters: int = 100000) -> dict:
+    """The matrix-core rate the device sustains with no memory traffic at all: the calibration
+    kernel (calib/mfma_rate.hip: back-to-back bf16 MFMAs whose operands are fragments of the
+    workload's own X and W1, two waves per SIMD) timed with HIP events right after the clock
+    run, in the same power state.  Under the socket power limit this, not the 2.5 PFLOP/s
+    spec, bounds what a GEMM on these operands can reach here; the rooflines report their
+    fraction of it."""
+    import ctypes
+    import torch
+    from megatron_tensor_transformer_linear_amd._build import CALIB_LIB_PATH
+    if not os.path.exists(CALIB_LIB_PATH):
+        return {"error": f"{CALIB_LIB_PATH} not built"}
+    lib = ctypes.CDLL(CALIB_LIB_PATH)
+    lib.tp_calib_mfma_loop.restype = ctypes.c_int
+    lib.tp_calib_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    nbytes = min(a_src.numel() * a_src.element_size(), b_src.numel() * b_src.element_size())
+    nbytes -= nbytes % 16
+    lib.tp_calib_mfma_flops.restype = ctypes.c_double
+    lib.tp_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus  # two 4-wave workgroups per CU: two waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    rates = []
+    for i in range(launches + 1):
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        rc = lib.tp_calib_mfma_loop(ctypes.c_void_p(a_src.data_ptr()),
+                                    ctypes.c_void_p(b_src.data_ptr()), nbytes,
+                                    ctypes.c_void_p(out.data_ptr()), blocks,
+                                    iters if i else iters // 10, ctypes.c_void_p(stream.cuda_stream))
+        e_.record(stream)
+        if rc != 0:
+            return {"error": f"tp_calib_mfma_loop returned {rc}"}
+        torch.cuda.synchronize()
+        if i:  # the first, shorter launch is a warm-up
+            rates.append(lib.tp_calib_mfma_flops(blocks, iters) / (s_.elapsed_time(e_) * 1e-3) / 1e12)
+    rates.sort()
+    return {"what": "bf16 MFMA loop, operands taken from the workload's X and W1, no memory "
+                    "traffic, two waves per SIMD (calib/mfma_rate.hip), timed right after the "
+                    "clock run",
+            "tflops": round(rates[len(rates) // 2], 1), "tflops_all": [round(r, 1) for r in rates],
+            "frac_of_spec": round(rates[len(rates) // 2] / PEAK_BF16_TFLOPS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -610,6 +659,8 @@ def main() -> int:
                     help="skip the cold-cache pass (each stage after a 512 MiB scratch write)")
     ap.add_argument("--no-clock", action="store_true",
                     help="do not sample the GPU clocks through amdsmi during the timed steps")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the matrix-core rate calibration run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain copy kernel over MIB mebibytes (reads and writes "
                          "MIB each), the known-size reference for HBM byte counters")
@@ -674,6 +725,11 @@ def main() -> int:
         clock = clock_leg(step, elapsed / args.steps * 1e3)
     sclk = (clock or {}).get("sclk_mhz") or {}
     sclk_ghz = sclk.get("median", 0) / 1e3 if sclk else None
+    ceiling = None
+    if not args.no_mfma_ceiling:
+        log("matrix-core rate calibration")
+        ceiling = mfma_ceiling_leg(dev, blk.X, blk.W1)
+    ceil_tf = (ceiling or {}).get("tflops")
 
     def avg_ms(key):  # per launch: the stage's event interval over its launches
         return float(np.mean([s.elapsed_time(e) for s, e in ev[key]])) / LAUNCHES[key]
@@ -732,6 +788,8 @@ def main() -> int:
              "time_per_step_ms": round(ms * LAUNCHES[key], 4)}
         if sclk_ghz:
             r["frac_at_measured_sclk"] = round(achieved / (PEAK_BF16_TFLOPS * sclk_ghz / 2.4), 4)
+        if ceil_tf:
+            r["frac_of_mfma_ceiling"] = round(achieved / ceil_tf, 4)
         rooflines[key] = r
     dominant = max(rooflines, key=lambda k: rooflines[k]["time_per_step_ms"])
 
@@ -760,6 +818,7 @@ def main() -> int:
         "roofline": rooflines[dominant],
         "rooflines": rooflines,
         "clock": clock,
+        "mfma_ceiling": ceiling,
         "stages": stages,
         # One simulated rank's layer shard (its attention-head shard and its MLP shard), the
         # unit the metric names: the rank's algorithmic flops over the sum of its stages'

@@ -1,8 +1,10 @@
 """Build of the gfx950 HIP library ``libtp_shard.so`` (in-tree, next to this file).
 
 Each ``csrc/*.hip`` source is compiled to an object with hipcc for gfx950 (in parallel),
-then the objects are linked into one shared library.  No GPU is needed: hipcc
-cross-compiles.  Packed-fp32 VALU instructions are disabled for all device code.
+then the objects are linked into one shared library.  The measurement library
+``libtp_calib.so`` (``calib/*.hip``: the matrix-core rate calibration the bench reports
+beside the GEMMs) is built the same way.  No GPU is needed: hipcc cross-compiles.
+Packed-fp32 VALU instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libtp_shard.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+CALIB_SRC = os.path.join(HERE, "calib")
+CALIB_LIB_PATH = os.path.join(HERE, "libtp_calib.so")
 
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -38,8 +42,8 @@ def hipcc_path() -> str:
 SOURCE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
 
 
-def sources() -> List[str]:
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources(folder: str = CSRC) -> List[str]:
+    return sorted(glob.glob(os.path.join(folder, "*.hip")))
 
 
 def _run(cmd: List[str]) -> None:
@@ -50,22 +54,29 @@ def _run(cmd: List[str]) -> None:
         raise RuntimeError(f"build step failed ({res.returncode}): {' '.join(cmd)}\n{out}")
 
 
-def build_library(jobs: Optional[int] = None, extra_flags: Optional[List[str]] = None) -> str:
-    """Compile every source and link LIB_PATH.  Always recompiles.  Returns the path."""
+def _build_one(srcs: List[str], lib_path: str, obj_dir: str, flags: List[str],
+               jobs: Optional[int]) -> str:
     hipcc = hipcc_path()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    flags = COMMON_FLAGS + list(extra_flags or [])
-    srcs = sources()
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.basename(s) + ".o") for s in srcs]
     jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1), 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_run, [hipcc] + flags + SOURCE_FLAGS.get(os.path.basename(s), [])
                           + ["-c", s, "-o", o]) for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build_library(jobs: Optional[int] = None, extra_flags: Optional[List[str]] = None) -> str:
+    """Compile every source and link LIB_PATH, then the calibration library CALIB_LIB_PATH.
+    Always recompiles.  Returns LIB_PATH."""
+    flags = COMMON_FLAGS + list(extra_flags or [])
+    _build_one(sources(), LIB_PATH, BUILD_DIR, flags, jobs)
+    _build_one(sources(CALIB_SRC), CALIB_LIB_PATH, os.path.join(BUILD_DIR, "calib"), flags, jobs)
     return LIB_PATH
 
 

@@ -52,6 +52,30 @@ def test_library_exports_every_declared_symbol(tp):
     assert set(tp.EXPORTED) == set(declared_functions())
 
 
+def test_calibration_library_loads_and_rejects_bad_arguments(tp):
+    """The bench's matrix-core rate calibration library is built beside the main one; bad
+    arguments are refused before any launch."""
+    from megatron_tensor_transformer_linear_amd import _build
+    assert os.path.exists(_build.CALIB_LIB_PATH)
+    lib = ctypes.CDLL(_build.CALIB_LIB_PATH)
+    lib.tp_calib_mfma_loop.restype = ctypes.c_int
+    lib.tp_calib_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.tp_calib_mfma_flops.restype = ctypes.c_double
+    lib.tp_calib_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is refused first
+    assert lib.tp_calib_mfma_loop(None, p, 4096, p, 512, 10, None) == -1
+    assert lib.tp_calib_mfma_loop(p, p, 4096, None, 512, 10, None) == -1
+    assert lib.tp_calib_mfma_loop(p, p, 4096, p, 0, 10, None) == -1
+    assert lib.tp_calib_mfma_loop(p, p, 4096, p, 512, 0, None) == -1
+    assert lib.tp_calib_mfma_loop(p, p, 4100, p, 512, 10, None) == -1
+    assert lib.tp_calib_mfma_loop(p, p, 0, p, 512, 10, None) == -1
+    assert lib.tp_calib_mfma_loop(ctypes.c_void_p(0x1008), p, 4096, p, 512, 10, None) == -1
+    # 512 workgroups x 4 waves x 10 rounds x 16 MFMAs x 32768 flops
+    assert lib.tp_calib_mfma_flops(512, 10) == 512 * 4 * 10 * 16 * 32768
+
+
 def test_status_strings(tp):
     for code in range(0, -10, -1):
         s = tp.tp_status_string(code)
