@@ -216,7 +216,7 @@ template <int BM, int BN, int NST, int EPI, int LAY>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   constexpr bool A_KC = (LAY & LAY_TN) == 0;  // A stored [M, K]
   constexpr bool B_KC = (LAY & LAY_NT) != 0;  // B stored as B^T [N, K]
-  // A K-contiguous operand is staged a pair of K steps at a time: pair p (steps 2p, 2p+1)
+  // A K-contiguous A operand is staged a pair of K steps at a time: pair p (steps 2p, 2p+1)
   // fills that operand's share of ring slots 2p and 2p+1 (mod NST), the first half of its
   // rows in slot 2p and the second half in slot 2p+1, each row as 128 contiguous bytes
   // (64 k).  A load then fetches whole 128-byte lines, where one K step of a row is half a
@@ -224,8 +224,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(GemmDesc g) {
   // stalled on them (a product whose operands are both K-contiguous ran 17 % slower than
   // the same product with neither).  Each wave's MFMA rows are one half, so a wave reads
   // one slot of the pair.
+  // A pair lands about 1.5 K steps after it is issued, a single-step stage about 3 (the
+  // ring holds 4 stages, so 2 pairs), so B (W^T in the input-gradient products) is staged
+  // one step at a time: MI355X, same call, dY 0.971 vs 1.010 ms and dX 0.949 vs 0.975 ms
+  // with both operands paired (1.03 and 1.06 ms with neither).
   constexpr bool A_PAIR = A_KC && KC_PAIRS;
-  constexpr bool B_PAIR = B_KC && KC_PAIRS;
+  constexpr bool B_PAIR = B_KC && KC_PAIRS && LAY != LAY_NT;
   static_assert(!(A_PAIR || B_PAIR) || NST == 4, "paired staging is scheduled for a 4-slot ring");
   using SA = OperandStage<BM, A_KC>;
   using SB = OperandStage<BN, B_KC>;
