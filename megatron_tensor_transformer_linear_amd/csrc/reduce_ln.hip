@@ -103,48 +103,77 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* v) {
 
 // FULL: every run of every thread lies inside the row (H == NCH * THREADS * 8), so no run
 // needs a bounds test and each batch of loads is issued without branches.
-template <int THREADS, int NCH, bool BF16, bool FULL>
+// PARTS: n_parts > 0; RES: a residual is given; LN: gamma is given (the LayerNorm runs).  They
+// are compile-time so that the row loop has no data-dependent branch around its loads: at
+// such a join the compiler waits for every load in flight, which would include the next
+// row's prefetched partial.
+template <int THREADS, int NCH, bool BF16, bool FULL, bool PARTS, bool RES, bool LN>
 __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   __shared__ float red[THREADS / 64];
   const int tid = threadIdx.x;
+  const int64_t H = r.H;
+  bool in[NCH];
+  int64_t col[NCH];
+  uint32_t boff[NCH];  // byte offset of the run in an fp32 row (past the row: out of range)
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    col[c] = ((int64_t)c * THREADS + tid) * 8;
+    in[c] = FULL || col[c] < H;
+    boff[c] = (uint32_t)col[c] * 4u;
+  }
+  const int np = r.n_parts;
+  // Partial p of row `row` into batch q: buffer loads from a resource spanning that row of the
+  // partial (wave-uniform, in scalar registers), at per-lane byte offsets shared by all
+  // partials; a row past the last has an empty range and reads as zeros.
+  auto load_part = [&](int64_t row, int p, f32x4_t (&q)[NCH][2]) __attribute__((always_inline)) {
+    const bool ok = row < r.rows;
+    const float* part = r.parts + (ok ? (int64_t)p * r.part_stride + row * H : 0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, ok ? (int)(H * 4) : 0, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, CPOL_NT));
+      q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, CPOL_NT));
+    }
+  };
+  // gamma and beta: for bf16 rows of up to 2048 runs they are loaded once per workgroup into
+  // LDS, where each thread reads back only the runs it wrote (per-thread storage: no barrier,
+  // 16 consecutive bytes per lane, no bank conflict); that keeps them out of the registers
+  // that hold the next row's prefetched partial.  Otherwise they are loaded per row.
+  constexpr bool GB_LDS = LN && BF16 && NCH * THREADS <= 2048;
+  __shared__ Raw8<BF16> gb_lds[GB_LDS ? 2 : 1][GB_LDS ? NCH * THREADS : 1];
+  if constexpr (GB_LDS) {
+    const void* beta = r.beta ? r.beta : r.gamma;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      Raw8<BF16> g{}, b{};
+      if (in[c]) {
+        g = load_raw8<BF16>(r.gamma, col[c]);
+        b = load_raw8<BF16>(beta, col[c]);
+      }
+      gb_lds[0][c * THREADS + tid] = g;
+      gb_lds[1][c * THREADS + tid] = b;
+    }
+  }
+  // Partial 0 of the workgroup's next row is loaded before the current row's residual,
+  // statistics and stores, so the row's tail never leaves the workgroup with no read in
+  // flight (the first row's comes before the loop).
+  f32x4_t qa[NCH][2], qb[NCH][2];
+  if constexpr (PARTS) load_part(blockIdx.x, 0, qa);
   for (int64_t row = blockIdx.x; row < r.rows; row += gridDim.x) {
-    const int64_t H = r.H;
     const int64_t roff = row * H;                              // inputs: dense rows
     const int64_t ooff = row * (r.ld_out > 0 ? r.ld_out : H);  // outputs: rows of pitch ld_out
 
-    bool in[NCH];
-    int64_t col[NCH];
-    uint32_t boff[NCH];  // byte offset of the run in an fp32 row (past the row: out of range)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      col[c] = ((int64_t)c * THREADS + tid) * 8;
-      in[c] = FULL || col[c] < H;
-      boff[c] = (uint32_t)col[c] * 4u;
-    }
-
     // h = sum of the partials in ascending order, then + residual.  Two register batches
     // alternate: the loads of partial p+1 go out before partial p is added, so one batch is
-    // always in flight while the other is summed.  The loads are buffer loads from a resource
-    // spanning the row of one partial (wave-uniform, in scalar registers), at per-lane byte
-    // offsets shared by all partials.  The loop body has no branch: a conditional use of a
-    // batch lets the compiler sink its loads behind the next batch's and wait for both; the
-    // last one or two partials are summed after it.
+    // always in flight while the other is summed.  The loop body has no branch: a conditional
+    // use of a batch lets the compiler sink its loads behind the next batch's and wait for
+    // both; the last one or two partials are summed after it.
     float v[NCH][8];
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
-    const int np = r.n_parts;
-    auto load_part = [&](int p, f32x4_t (&q)[NCH][2]) {
-      const float* part = r.parts + (int64_t)p * r.part_stride + roff;
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, (int)(H * 4), 0x00020000);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, CPOL_NT));
-        q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, CPOL_NT));
-      }
-    };
     auto add_part = [&](const f32x4_t (&q)[NCH][2]) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
@@ -154,24 +183,22 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
           v[c][4 + e] += q[c][1][e];
         }
     };
-    if (np > 0) {
-      f32x4_t qa[NCH][2], qb[NCH][2];
+    if constexpr (PARTS) {
       // The scheduling barriers keep each batch's loads ahead of the previous batch's adds
       // (the scheduler would otherwise move the adds up and wait with nothing in flight).
-      load_part(0, qa);
       int p = 0;
       for (; p + 2 < np; p += 2) {
-        load_part(p + 1, qb);
+        load_part(row, p + 1, qb);
         __builtin_amdgcn_sched_barrier(0);
         add_part(qa);
         __builtin_amdgcn_sched_barrier(0);
-        load_part(p + 2, qa);
+        load_part(row, p + 2, qa);
         __builtin_amdgcn_sched_barrier(0);
         add_part(qb);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (p + 1 < np) {
-        load_part(p + 1, qb);
+        load_part(row, p + 1, qb);
         __builtin_amdgcn_sched_barrier(0);
         add_part(qa);
         __builtin_amdgcn_sched_barrier(0);
@@ -180,17 +207,36 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
         add_part(qa);
       }
     }
+    // The row's other loads (residual, gamma, beta) go out before the next row's first partial:
+    // the vector-memory counter completes in order, so waiting for a load issued after the
+    // prefetch would also wait for the prefetch.  beta NULL reads gamma's values and uses 0.
     Raw8<BF16> res[NCH];
-    if (r.residual) {
+    if constexpr (RES) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         if (in[c]) res[c] = load_raw8<BF16>(r.residual, roff + col[c]);
+    }
+    Raw8<BF16> gm[NCH], bt[NCH];
+    if constexpr (LN && !GB_LDS) {
+      const void* beta = r.beta ? r.beta : r.gamma;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (in[c]) {
+          gm[c] = load_raw8<BF16>(r.gamma, col[c]);
+          bt[c] = load_raw8<BF16>(beta, col[c]);
+        }
+      }
+    }
+    if constexpr (PARTS) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_part(row + gridDim.x, 0, qa);
+      __builtin_amdgcn_sched_barrier(0);
     }
     float sum = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (in[c]) {
-        if (r.residual) {
+        if constexpr (RES) {
           float x[8];
           unpack8<BF16>(res[c], x);
 #pragma unroll
@@ -206,17 +252,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2) sum += v[c][e] + v[c][e + 1];
     }
-    if (!r.gamma) continue;
-
-    // gamma / beta go out before the statistics' reductions hide their latency.
-    Raw8<BF16> gm[NCH], bt[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (in[c]) {
-        gm[c] = load_raw8<BF16>(r.gamma, col[c]);
-        if (r.beta) bt[c] = load_raw8<BF16>(r.beta, col[c]);
-      }
-    }
+    if constexpr (!LN) continue;
     const float inv_h = 1.0f / (float)H;
     const float mean = block_sum<THREADS>(sum, red) * inv_h;
     float sq = 0.0f;
@@ -236,9 +272,14 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
     for (int c = 0; c < NCH; ++c) {
       if (in[c]) {
         float gv[8], bv[8];
-        unpack8<BF16>(gm[c], gv);
-        if (r.beta) unpack8<BF16>(bt[c], bv);
-        else
+        if constexpr (GB_LDS) {
+          unpack8<BF16>(gb_lds[0][c * THREADS + tid], gv);
+          unpack8<BF16>(gb_lds[1][c * THREADS + tid], bv);
+        } else {
+          unpack8<BF16>(gm[c], gv);
+          unpack8<BF16>(bt[c], bv);
+        }
+        if (!r.beta)
 #pragma unroll
           for (int e = 0; e < 8; ++e) bv[e] = 0.0f;
         F8 y;
@@ -417,8 +458,17 @@ hipError_t launch_variant(const ReduceDesc& r, hipStream_t stream) {
     }
   }
   const int64_t blocks = min(r.rows, (int64_t)16 * cus);
-  hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, BF16, FULL>), dim3((unsigned)blocks),
-                     dim3(THREADS), 0, stream, r);
+  const dim3 grid((unsigned)blocks), block(THREADS);
+  const bool parts = r.n_parts > 0, res = r.residual != nullptr, ln = r.gamma != nullptr;
+#define TPK_REDUCE_LAUNCH(P, R, L) \
+  hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, BF16, FULL, P, R, L>), grid, block, 0, stream, r)
+  if (parts && res && ln) TPK_REDUCE_LAUNCH(true, true, true);
+  else if (parts && res) TPK_REDUCE_LAUNCH(true, true, false);
+  else if (parts && ln) TPK_REDUCE_LAUNCH(true, false, true);
+  else if (parts) TPK_REDUCE_LAUNCH(true, false, false);
+  else if (ln) TPK_REDUCE_LAUNCH(false, true, true);  // no partials: the residual is required
+  else TPK_REDUCE_LAUNCH(false, true, false);
+#undef TPK_REDUCE_LAUNCH
   return hipGetLastError();
 }
 
