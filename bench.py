@@ -20,7 +20,7 @@ clocks are sampled through amdsmi over a separate ~6 s run of the same steps, an
 fractions of peak are also given at that graphics clock, and against the matrix-core rate the
 device sustains with no memory traffic at all in the same power state (`mfma_ceiling`: a
 calibration loop of MFMAs on random operands).  A cold-cache pass then times every
-stage again after writing 512 MiB of scratch (twice the 256 MB Infinity Cache) just before
+stage again after reading 512 MiB of scratch (twice the 256 MB Infinity Cache) just before
 it, so nothing it reads is cached (`stages[*].cold_*`).  The CPU baseline times the float64
 oracle on a bounded row sample of the same workload on this host, and the full oracle of each
 other workload.  After the timed steps, the sequence-parallel form of the epilogue (each
@@ -56,7 +56,7 @@ PEAK_F32_MFMA_TFLOPS = 157.3  # dense fp32 MFMA
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_block_bf16_tp8_hbm_traffic.md")
-FLUSH_MIB = 512  # scratch written before each cold-cache stage: 2x the 256 MB Infinity Cache
+FLUSH_MIB = 512  # scratch read before each cold-cache stage: 2x the 256 MB Infinity Cache
 
 
 def log(msg: str) -> None:
@@ -182,17 +182,20 @@ class ClockSampler:
 
 
 class CacheFlush:
-    """Writes FLUSH_MIB MiB of scratch (one fill kernel) on the current stream, evicting
-    everything a following kernel reads from the L2s and the 256 MB Infinity Cache."""
+    """Reads FLUSH_MIB MiB of scratch (one reduction kernel) on the current stream, evicting
+    everything a following kernel reads from the L2s and the 256 MB Infinity Cache.  A read
+    sweep leaves the caches holding clean lines: a write sweep (a fill) would leave up to
+    256 MB of dirty lines whose write-back then runs during the timed stage and is charged
+    to it (it doubled the pre-LayerNorm's cold time)."""
 
     def __init__(self, dev, mib: int = FLUSH_MIB):
         import torch
-        self.buf = torch.empty(mib << 18, dtype=torch.float32, device=dev)
-        self.i = 0
+        self.buf = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros((), dtype=torch.float32, device=dev)
 
     def __call__(self):
-        self.i += 1
-        self.buf.fill_(float(self.i))
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def cpu_baseline(cfg, t, qkv_vals) -> dict:
@@ -413,7 +416,7 @@ def clock_leg(step, ms_per_step: float, seconds: float = 6.0) -> dict:
 
 def cold_stages(cfg, blk, stream, flush, n_steps: int) -> dict:
     """Each stage of the block step after a cache flush: per step, for every stage in order,
-    FLUSH_MIB MiB of scratch are written, then the stage runs between two events.  The stage's
+    FLUSH_MIB MiB of scratch are read, then the stage runs between two events.  The stage's
     first launch therefore finds nothing of its operands cached (later launches of a stage,
     the 8 ranks back to back, see what the earlier ones left, as in the step).  Returns the
     per-launch milliseconds of each stage, averaged over n_steps."""
@@ -472,7 +475,7 @@ def other_workloads_leg(dev, steps: int = 5, flush=None, cpu: bool = True) -> di
     each).  Each stage runs for every rank back to back, with HIP events only at the stage
     boundaries; 1 untimed step, then `steps` timed ones.  Per-rank times are a stage's
     interval over its rank count.  With `flush`, a second pass times each stage again with
-    the scratch written just before it (the `cold_` figures; the others are warm: each stage
+    the scratch read just before it (the `cold_` figures; the others are warm: each stage
     follows the previous one).  With `cpu`, the float64 oracle of the whole workload is timed
     on this host (`cpu_oracle`)."""
     import torch
@@ -656,7 +659,7 @@ def main() -> int:
     ap.add_argument("--no-fold", action="store_true",
                     help="skip the measurement of the step with folded reduces")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache pass (each stage after a 512 MiB scratch write)")
+                    help="skip the cold-cache pass (each stage after a 512 MiB scratch read)")
     ap.add_argument("--no-clock", action="store_true",
                     help="do not sample the GPU clocks through amdsmi during the timed steps")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
