@@ -87,16 +87,3 @@ def sample_rows(T: int, seq: int, seed: int, n_random: int = 6):
     rows |= set(int(x) for x in rng.integers(0, T, n_random))
     return np.array(sorted(rows))
 
-
-def block_rows(T: int, seq: int, seed: int, block: int = 128):
-    """One seeded row in every block of `block` rows (the attention kernel's query blocks; two
-    per 256-row GEMM tile), plus the first and last row of every sequence and of the whole
-    input: every output tile and every sequence boundary is sampled."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    rows = {0, T - 1}
-    for b0 in range(0, T, block):
-        rows.add(int(b0 + rng.integers(0, min(block, T - b0))))
-    if seq:
-        for b in range(T // seq):
-            rows |= {b * seq, b * seq + seq - 1}
-    return np.array(sorted(rows))
