@@ -358,6 +358,42 @@ def test_column_edge_shapes(lib, dtype, T, H, N, world, rank):
     check("column", Y[:, :nl], O.col_linear(Xv, Wv, rank, world, "gelu_tanh"), dtype)
 
 
+@pytest.mark.parametrize("T,N", [(448, 512), (512, 512), (64, 8), (1000, 40)])
+def test_f32_small_and_tiled_kernels_integer_exact(lib, T, N):
+    """The fp32 products take a 16 x 16-tile kernel with the contraction split over its waves
+    when there are fewer 64 x 64 tiles than a quarter of the compute units (448 x 512: 56
+    tiles), and the 64 x 64 tile otherwise (512 x 512: 64 tiles).  With integer operands every
+    sum is exact in any order, so both must equal the oracle bit for bit: the column product
+    with its GeLU off, and the row partial written and then accumulated onto itself (its
+    fold epilogue).  K = 776 ends inside a 256-deep block of the split kernel."""
+    tp, pl = lib
+    K = 776
+    rng = np.random.Generator(np.random.PCG64(3000 + T + N))
+    X = integer_matrix(rng, (T, K), -1, 1, "f32")
+    W = integer_matrix(rng, (K, 2 * N), -2, 2, "f32")
+    Xd, Wd = dev(X), dev(W)
+    Xv, Wv = X.values(), W.values()
+    Y = torch.full((T, N), -5.0, dtype=torch.float32, device="cuda:0")
+    say(f"  fp32 kernels T={T} K={K} N={N}: column rank 1 of 2")
+    tp.tp_col_linear_gelu(Xd, Wd, Y, N, T, K, 2 * N, 1, 2, tp.TP_ACT_NONE, tp.TP_F32)
+    _sync()
+    check_exact("column rank 1", Y, O.col_linear(Xv, Wv, 1, 2), "f32")
+    # row product: the full input [T, 2K] (rank 1's shard is its column block 1) against
+    # W [2K, N]; the call reads the shard in place (leading dimension 2K)
+    Xf = integer_matrix(rng, (T, 2 * K), -1, 1, "f32")
+    Wr = integer_matrix(rng, (2 * K, N), -2, 2, "f32")
+    Xfd, Wrd = dev(Xf), dev(Wr)
+    Z = torch.empty(T, N, dtype=torch.float32, device="cuda:0")
+    say(f"  fp32 kernels T={T} K={K} N={N}: row partial rank 1 of 2, then accumulated")
+    tp.tp_row_linear_partial(Xfd[:, K:], 2 * K, Wrd, Z, T, 2 * K, N, 1, 2, tp.TP_F32)
+    _sync()
+    part = O.row_linear_partial(Xf.values(), Wr.values(), 1, 2)
+    check_exact("row partial rank 1", Z, part, "f32")
+    tp.tp_row_linear_fold(Xfd[:, K:], 2 * K, Wrd, Z, T, 2 * K, N, 1, 2, 1, tp.TP_F32)
+    _sync()
+    check_exact("row partial accumulated", Z, 2 * part, "f32")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("T,K,N,world,rank", [
     (1, 8, 8, 1, 0),
