@@ -28,7 +28,8 @@ rank's reduce-scatter of its 1024 rows) and the backward pass of the MLP pair (t
 gradient products of every rank and the reduce of the input-gradient partials; --no-backward
 skips it) are timed on their own and reported beside the step, outside `value`, and so is the
 same step with each epilogue's reduce folded into the row-parallel products (one fp32 running
-sum instead of 8 stacked partials; --no-fold skips it).  The other workloads of the path (the
+sum instead of 8 stacked partials) and with the 8 partials stored in bf16 (--no-fold skips
+both).  The other workloads of the path (the
 fp32 MLP, the single linear, the bf16 MLP shard and the attention-head shard) are timed the
 same way and reported per rank under `other_workloads` (--no-workloads skips them).
 """
@@ -292,18 +293,23 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
     return out
 
 
-def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
-    """The same block step with the reduce folded into the row-parallel products (each rank's
-    output projection and MLP row GEMM add their partial to one fp32 running sum in ascending
-    rank order; the epilogues then read one partial instead of 8).  Same weights and inputs as
-    the timed step; the outputs are bit-identical to it."""
+def folded_block_leg(cfg, blk, stream, steps: int, variant: str = "fold") -> dict:
+    """The same block step in one of the two variants of the exchange, with the same weights
+    and inputs as the timed step:
+      fold:   the reduce folded into the row-parallel products (each rank's output projection
+              and MLP row GEMM add their partial to one fp32 running sum in ascending rank
+              order; the epilogues then read one partial instead of 8); the outputs are
+              bit-identical to the timed step's;
+      bf16:   the 8 partials stored in bf16 (each rounded once), the epilogues reading half
+              the bytes; the outputs differ from the timed step's by that rounding."""
     import torch
     from megatron_tensor_transformer_linear_amd import pipeline as pl
     from workloads.configs import rank_flops, reduce_bytes
 
+    fold = variant == "fold"
     fb = pl.BlockShard(blk.X, blk.Wqkv, blk.Wo, blk.W1, blk.W2, blk.g1, blk.b1, blk.g2, blk.b2,
                        cfg.world, cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, True, cfg.eps,
-                       fold=True)
+                       fold=fold, bf16_partials=not fold)
     ev = {k: [] for k in LAUNCHES}
     step = stage_step(cfg, fb, stream, ev)
 
@@ -317,8 +323,9 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
     fl = rank_flops(cfg)
     step_flops = cfg.world * sum(fl.values())
     T, H = cfg.tokens, cfg.hidden
-    r1 = reduce_bytes(T, H, 1, "bf16", residual=True, h_out=True, y_out=True)
-    r2 = reduce_bytes(T, H, 1, "bf16", residual=True, h_out=True, y_out=False)
+    n_parts, pdt = (1, "f32") if fold else (cfg.world, "bf16")
+    r1 = reduce_bytes(T, H, n_parts, "bf16", residual=True, h_out=True, y_out=True, parts_dtype=pdt)
+    r2 = reduce_bytes(T, H, n_parts, "bf16", residual=True, h_out=True, y_out=False, parts_dtype=pdt)
 
     def avg_ms(key):  # per launch
         return float(np.mean([s.elapsed_time(e) for s, e in ev[key]])) / LAUNCHES[key]
@@ -326,7 +333,10 @@ def folded_block_leg(cfg, blk, stream, steps: int) -> dict:
     out = {
         "what": ("the block step with each epilogue's reduce folded into the row-parallel "
                  "products' epilogues (one fp32 running sum, ranks added in ascending order); "
-                 "bit-identical outputs"),
+                 "bit-identical outputs" if fold else
+                 "the block step with every rank's partial stored in bf16 (the exchanged "
+                 "activation at 2 bytes per element), summed in fp32; outputs differ from the "
+                 "timed step's by the partials' rounding"),
         "steps": steps,
         "ms_per_step": round(elapsed / steps * 1e3, 3),
         "tflops": round(step_flops * steps / elapsed / 1e12, 2),
@@ -664,7 +674,8 @@ def main() -> int:
                     help="skip the measurement of the other workloads (fp32 MLP, single linear, "
                          "bf16 MLP shard, attention-head shard)")
     ap.add_argument("--no-fold", action="store_true",
-                    help="skip the measurement of the step with folded reduces")
+                    help="skip the measurements of the step with folded reduces and with "
+                         "bf16 partials")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (each stage after a 512 MiB scratch read)")
     ap.add_argument("--no-clock", action="store_true",
@@ -871,6 +882,9 @@ def main() -> int:
     if not args.no_fold:
         log("timing the block step with folded reduces")
         result["folded_step"] = folded_block_leg(cfg, blk, stream, max(1, min(args.steps, 5)))
+        log("timing the block step with bf16 partials")
+        result["bf16_partials_step"] = folded_block_leg(cfg, blk, stream,
+                                                        max(1, min(args.steps, 5)), "bf16")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a row sample")
         result["cpu_baseline"] = cpu_baseline(cfg, t, np.hstack(

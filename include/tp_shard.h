@@ -123,6 +123,20 @@ int tp_row_linear_fold(const void* X, int64_t ldx, const void* W, float* Zsum,
                        int64_t seq, int64_t K, int64_t N, int rank, int world,
                        int accumulate, int dtype, void* stream);
 
+/* Row-parallel linear with bf16 partials, the exchange as the pages count it (pwwt.cn
+ * section 5.2: the all-reduce's [S, H] input at 2 bytes per element, BF16; section 6.3: the
+ * summation order and BF16 arithmetic as sources of error between TP and one device).
+ * Zpart[t, n] is the fp32 sum of tp_row_linear_partial,
+ * rounded once to bf16 (nearest, ties to even) and written as a dense bf16 [seq, N] block;
+ * tp_partial_reduce_residual_ln_bf16 then reads half the bytes of the fp32 partials.  The
+ * partials' rounding adds to the error of the reduced sum (relative to its partials, 2^-9 per
+ * partial), so this is a variant beside the fp32-partial path, not a replacement.  Inputs are
+ * bf16 (no dtype argument); X, ldx, W, shard addressing and errors are those of
+ * tp_row_linear_partial (TP_ERR_DTYPE does not occur). */
+int tp_row_linear_partial_bf16(const void* X, int64_t ldx, const void* W, void* Zpart,
+                               int64_t seq, int64_t K, int64_t N, int rank, int world,
+                               void* stream);
+
 /* Column-parallel linear + GeLU that also keeps the pre-activation for the backward pass:
  * exactly tp_col_linear_gelu with act = TP_ACT_GELU_TANH, plus
  *
@@ -231,6 +245,16 @@ int tp_attn_head_shard_fold(const void* Xn, const void* Wqkv, const void* Wo, fl
                             int rank, int world, int causal, int accumulate, int dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention-head shard with a bf16 partial (the bf16-partial variant of
+ * tp_row_linear_partial_bf16 for the output projection): Zpart [batch*seq, H] receives the
+ * fp32 A_r . Wo[rank rows, :] of tp_attn_head_shard rounded once to bf16.  Inputs are bf16
+ * (no dtype argument); all other arguments, the workspace contents and the errors are those
+ * of tp_attn_head_shard. */
+int tp_attn_head_shard_bf16(const void* Xn, const void* Wqkv, const void* Wo, void* Zpart,
+                            int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                            int rank, int world, int causal, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Bytes of the library's own scratch array (one per GPU) that tp_attn_head_shard_noalloc uses
  * as its workspace: 160 MiB, what tp_attn_workspace_bytes gives for one rank of the largest
  * workload served (8192 tokens, 12 heads of 128 per rank, H = 12288, on 256 compute units:
@@ -279,6 +303,18 @@ int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_
                                   const void* residual, const void* gamma, const void* beta,
                                   float eps, void* h_out, void* y_out,
                                   int64_t rows, int64_t H, int dtype, void* stream);
+
+/* tp_partial_reduce_residual_ln over bf16 partials (those of tp_row_linear_partial_bf16 and
+ * tp_attn_head_shard_bf16): each partial is widened to fp32 and the sum, residual add and
+ * LayerNorm are those of the fp32-partial call, in the same order.  parts: n_parts dense bf16
+ * [rows, H] blocks, block p at parts + p*part_stride elements (part_stride >= rows*H and a
+ * multiple of 8 when n_parts > 1).  residual, gamma, beta, h_out and y_out are bf16.  Other
+ * arguments and errors are those of tp_partial_reduce_residual_ln (no dtype argument, so no
+ * TP_ERR_DTYPE). */
+int tp_partial_reduce_residual_ln_bf16(const void* parts, int n_parts, int64_t part_stride,
+                                       const void* residual, const void* gamma, const void* beta,
+                                       float eps, void* h_out, void* y_out,
+                                       int64_t rows, int64_t H, void* stream);
 
 /* Sequence-parallel form of the same epilogue: the reduce-scatter of rank `rank`, fused with
  * the residual add and LayerNorm of that rank's rows (pwwt.cn section 5.1, figure 7: an

@@ -83,7 +83,7 @@ struct AttnDesc {
 
 // h = residual + sum_p parts[p]; y = LayerNorm(h) * gamma + beta.
 struct ReduceDesc {
-  const float* parts;
+  const float* parts;  // fp32 partials, or bf16 ones (parts_bf16) at the same address
   int n_parts;
   int64_t part_stride;
   const void* residual;
@@ -95,6 +95,7 @@ struct ReduceDesc {
   int64_t rows, H;
   int bf16;  // io dtype is bf16 (else fp32)
   int64_t ld_out = 0;  // row pitch of h_out and y_out in elements (0: H)
+  int parts_bf16 = 0;  // the partials are bf16 (bf16 io only)
 };
 
 // Tile shapes of one bf16 product: columns [0, n0) with bm0 x bn0 tiles, then, if n1 > 0,

@@ -107,7 +107,8 @@ __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* v) {
 // are compile-time so that the row loop has no data-dependent branch around its loads: at
 // such a join the compiler waits for every load in flight, which would include the next
 // row's prefetched partial.
-template <int THREADS, int NCH, bool BF16, bool FULL, bool PARTS, bool RES, bool LN>
+// PB: the partials are bf16 (16 bytes per run of 8), summed in fp32 exactly as fp32 ones.
+template <int THREADS, int NCH, bool BF16, bool FULL, bool PARTS, bool RES, bool LN, bool PB = false>
 __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   __shared__ float red[THREADS / 64];
   const int tid = threadIdx.x;
@@ -125,15 +126,21 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   // Partial p of row `row` into batch q: buffer loads from a resource spanning that row of the
   // partial (wave-uniform, in scalar registers), at per-lane byte offsets shared by all
   // partials; a row past the last has an empty range and reads as zeros.
+  // (bf16 partials: the 16 bytes of a run in q[c][0], as raw bits)
+  constexpr int PES = PB ? 2 : 4;  // bytes per element of a partial
   auto load_part = [&](int64_t row, int p, f32x4_t (&q)[NCH][2]) __attribute__((always_inline)) {
     const bool ok = row < r.rows;
-    const float* part = r.parts + (ok ? (int64_t)p * r.part_stride + row * H : 0);
+    const char* part = (const char*)r.parts + (ok ? ((int64_t)p * r.part_stride + row * H) * PES : 0);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, ok ? (int)(H * 4) : 0, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)part, (short)0, ok ? (int)(H * PES) : 0, 0x00020000);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, CPOL_NT));
-      q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, CPOL_NT));
+      if constexpr (PB) {
+        q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] / 2, 0, CPOL_NT));
+      } else {
+        q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, CPOL_NT));
+        q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, CPOL_NT));
+      }
     }
   };
   // gamma and beta: for bf16 rows of up to 2048 runs they are loaded once per workgroup into
@@ -176,12 +183,22 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
       for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
     auto add_part = [&](const f32x4_t (&q)[NCH][2]) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
+      for (int c = 0; c < NCH; ++c) {
+        if constexpr (PB) {
+          Raw8<true> raw;
+          raw.u = __builtin_bit_cast(uint4, q[c][0]);
+          float x[8];
+          unpack8<true>(raw, x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[c][e] += q[c][0][e];
-          v[c][4 + e] += q[c][1][e];
+          for (int e = 0; e < 8; ++e) v[c][e] += x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[c][e] += q[c][0][e];
+            v[c][4 + e] += q[c][1][e];
+          }
         }
+      }
     };
     if constexpr (PARTS) {
       // The scheduling barriers keep each batch's loads ahead of the previous batch's adds
@@ -460,6 +477,19 @@ hipError_t launch_variant(const ReduceDesc& r, hipStream_t stream) {
   const int64_t blocks = min(r.rows, (int64_t)16 * cus);
   const dim3 grid((unsigned)blocks), block(THREADS);
   const bool parts = r.n_parts > 0, res = r.residual != nullptr, ln = r.gamma != nullptr;
+  if constexpr (BF16) {
+    if (parts && r.parts_bf16) {
+#define TPK_REDUCE_LAUNCH_PB(R, L) \
+  hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, true, FULL, true, R, L, true>), grid, block, 0, stream, r)
+      if (res && ln) TPK_REDUCE_LAUNCH_PB(true, true);
+      else if (res) TPK_REDUCE_LAUNCH_PB(true, false);
+      else if (ln) TPK_REDUCE_LAUNCH_PB(false, true);
+      else TPK_REDUCE_LAUNCH_PB(false, false);
+#undef TPK_REDUCE_LAUNCH_PB
+      return hipGetLastError();
+    }
+  }
+  if (r.parts_bf16 && parts) return hipErrorInvalidValue;  // bf16 partials need bf16 io
 #define TPK_REDUCE_LAUNCH(P, R, L) \
   hipLaunchKernelGGL((reduce_ln_kernel<THREADS, NCH, BF16, FULL, P, R, L>), grid, block, 0, stream, r)
   if (parts && res && ln) TPK_REDUCE_LAUNCH(true, true, true);

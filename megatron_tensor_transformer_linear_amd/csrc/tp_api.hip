@@ -65,9 +65,9 @@ int attn_sizes(int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
   return TP_OK;
 }
 
-// Rank `rank`'s row-parallel product into the fp32 Z [seq, N]: written (EPI_PARTIAL_F32) or
-// added to what Z holds (EPI_ACC_F32).
-int row_linear(const void* X, int64_t ldx, const void* W, float* Z, int64_t seq, int64_t K,
+// Rank `rank`'s row-parallel product into Z [seq, N]: fp32, written (EPI_PARTIAL_F32) or
+// added to what Z holds (EPI_ACC_F32); or bf16, written (EPI_STORE, bf16 io only).
+int row_linear(const void* X, int64_t ldx, const void* W, void* Z, int64_t seq, int64_t K,
                int64_t N, int rank, int world, int epi, int dtype, void* stream) {
   if (!X || !W || !Z) return TP_ERR_NULL;
   if (dtype != TP_F32 && dtype != TP_BF16) return TP_ERR_DTYPE;
@@ -101,8 +101,8 @@ int row_linear(const void* X, int64_t ldx, const void* W, float* Z, int64_t seq,
 }
 
 // Rank `rank`'s attention head shard; its output projection writes (EPI_PARTIAL_F32) or adds
-// to (EPI_ACC_F32) the fp32 Z [batch*seq, H].
-int attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
+// to (EPI_ACC_F32) the fp32 Z [batch*seq, H], or writes it in bf16 (EPI_STORE).
+int attn_head_shard(const void* Xn, const void* Wqkv, const void* Wo, void* Zpart,
                     int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim, int rank,
                     int world, int causal, int epi, int dtype, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -258,6 +258,12 @@ int tp_row_linear_fold(const void* X, int64_t ldx, const void* W, float* Zsum, i
                        void* stream) {
   return row_linear(X, ldx, W, Zsum, seq, K, N, rank, world,
                     accumulate ? EPI_ACC_F32 : EPI_PARTIAL_F32, dtype, stream);
+}
+
+int tp_row_linear_partial_bf16(const void* X, int64_t ldx, const void* W, void* Zpart,
+                               int64_t seq, int64_t K, int64_t N, int rank, int world,
+                               void* stream) {
+  return row_linear(X, ldx, W, Zpart, seq, K, N, rank, world, EPI_STORE, TP_BF16, stream);
 }
 
 int tp_col_linear_gelu_save(const void* X, const void* W, void* Y, int64_t ldy, void* U,
@@ -449,6 +455,14 @@ int tp_attn_head_shard_fold(const void* Xn, const void* Wqkv, const void* Wo, fl
                          workspace_bytes, stream);
 }
 
+int tp_attn_head_shard_bf16(const void* Xn, const void* Wqkv, const void* Wo, void* Zpart,
+                            int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
+                            int rank, int world, int causal, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return attn_head_shard(Xn, Wqkv, Wo, Zpart, batch, seq, H, n_heads, head_dim, rank, world,
+                         causal, EPI_STORE, TP_BF16, workspace, workspace_bytes, stream);
+}
+
 int tp_attn_head_shard_noalloc(const void* Xn, const void* Wqkv, const void* Wo, float* Zpart,
                                int64_t batch, int64_t seq, int64_t H, int n_heads, int head_dim,
                                int rank, int world, int causal, int dtype, void* stream) {
@@ -500,6 +514,42 @@ int tp_partial_reduce_residual_ln(const float* parts, int n_parts, int64_t part_
   r.rows = rows;
   r.H = H;
   r.bf16 = dtype == TP_BF16;
+  (void)hipGetLastError();
+  return launched(launch_reduce_ln(r, (hipStream_t)stream));
+}
+
+int tp_partial_reduce_residual_ln_bf16(const void* parts, int n_parts, int64_t part_stride,
+                                       const void* residual, const void* gamma, const void* beta,
+                                       float eps, void* h_out, void* y_out, int64_t rows,
+                                       int64_t H, void* stream) {
+  if (n_parts < 0) return TP_ERR_SHAPE;
+  if (n_parts > 0 && !parts) return TP_ERR_NULL;
+  if (n_parts == 0 && !residual) return TP_ERR_NULL;
+  if (gamma && !y_out) return TP_ERR_NULL;
+  if (!gamma && !h_out) return TP_ERR_NULL;
+  if (rows <= 0 || rows > INT32_MAX || H <= 0 || H > 65536) return TP_ERR_SHAPE;
+  if (!(eps >= 0.0f) || isinf(eps)) return TP_ERR_SHAPE;
+  if (n_parts > 1 && part_stride < rows * H) return TP_ERR_SHAPE;
+  if (!mult8(H)) return TP_ERR_ALIGN;
+  if (n_parts > 1 && !mult8(part_stride)) return TP_ERR_ALIGN;
+  const void* ptrs[] = {parts, residual, gamma, beta, h_out, y_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return TP_ERR_ALIGN;
+
+  ReduceDesc r;
+  r.parts = (const float*)parts;  // read as bf16 (parts_bf16)
+  r.n_parts = n_parts;
+  r.part_stride = part_stride;
+  r.residual = residual;
+  r.gamma = gamma;
+  r.beta = beta;
+  r.eps = eps;
+  r.h_out = h_out;
+  r.y_out = gamma ? y_out : nullptr;
+  r.rows = rows;
+  r.H = H;
+  r.bf16 = 1;
+  r.parts_bf16 = 1;
   (void)hipGetLastError();
   return launched(launch_reduce_ln(r, (hipStream_t)stream));
 }

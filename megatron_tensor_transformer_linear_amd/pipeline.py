@@ -68,7 +68,8 @@ class MLPShard:
         self.Yfull = torch.empty(self.T, self.F, dtype=torch_dtype(dtype), device=dev)
         # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
         self.n_parts = 1 if fold else world
-        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
+        self.parts = torch.empty(self.n_parts, self.T, self.H,
+                                 dtype=bf if bf16_partials else torch.float32, device=dev)
         if residual_ln:
             self.h = torch.empty(self.T, self.H, dtype=torch_dtype(dtype), device=dev)
             self.y = torch.empty_like(self.h)
@@ -256,7 +257,8 @@ class AttnShard:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
         self.n_parts = 1 if fold else world
-        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
+        self.parts = torch.empty(self.n_parts, self.T, self.H,
+                                 dtype=bf if bf16_partials else torch.float32, device=dev)
         self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
 
     def workspace_views(self):
@@ -300,12 +302,17 @@ class BlockShard:
     fold=True folds the reduce into the row-parallel products: rank 0's output projection
     writes one fp32 [T, H] running sum and ranks 1..P-1 add to it in ascending order, so each
     epilogue reads one partial instead of P (pwwt.cn sections 2.3, 5.3).  The additions are
-    the stacked reduce's, in its order, so every output is bit-identical."""
+    the stacked reduce's, in its order, so every output is bit-identical.
+
+    bf16_partials=True stores every rank's partial in bf16, as the pages count the exchanged
+    [S, H] partial (pwwt.cn section 5.2: 2 bytes per element): each partial is rounded once
+    and the reduces read half the bytes; the sums, residual adds and LayerNorms are the
+    fp32-partial path's."""
 
     def __init__(self, X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, world: int,
                  batch: int, seq: int, n_heads: int, head_dim: int, causal: bool = True,
                  eps: float = 1e-5, stream=None, sequence_parallel: bool = False,
-                 fold: bool = False):
+                 fold: bool = False, bf16_partials: bool = False):
         self.X, self.Wqkv, self.Wo, self.W1, self.W2 = X, Wqkv, Wo, W1, W2
         self.g1, self.b1, self.g2, self.b2 = gamma1, beta1, gamma2, beta2
         self.T, self.H = X.shape
@@ -315,6 +322,9 @@ class BlockShard:
         self.stream = stream
         self.sequence_parallel = sequence_parallel
         self.fold = fold
+        self.bf16_partials = bf16_partials
+        if bf16_partials and (fold or sequence_parallel):
+            raise ValueError("bf16 partials are built for the stacked epilogue only")
         if sequence_parallel and self.T % world:
             raise ValueError("sequence parallelism needs tokens divisible by the world size")
         dev = X.device
@@ -328,7 +338,8 @@ class BlockShard:
         self.Yr = torch.empty(world, self.T, self.F // world, dtype=bf, device=dev)
         # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
         self.n_parts = 1 if fold else world
-        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
+        self.parts = torch.empty(self.n_parts, self.T, self.H,
+                                 dtype=bf if bf16_partials else torch.float32, device=dev)
         self.ws_bytes = tp.tp_attn_workspace_bytes(batch, seq, self.H, n_heads, head_dim, world,
                                                    tp.TP_BF16)
         if self.ws_bytes == 0:
@@ -346,6 +357,11 @@ class BlockShard:
                                        int(self.causal), int(r > 0), tp.TP_BF16, self.ws,
                                        self.ws_bytes, self.stream)
             return
+        if self.bf16_partials:
+            tp.tp_attn_head_shard_bf16(self.xn, self.Wqkv, self.Wo, self.parts[r], self.batch,
+                                       self.seq, self.H, self.nh, self.d, r, self.P,
+                                       int(self.causal), self.ws, self.ws_bytes, self.stream)
+            return
         tp.tp_attn_head_shard(self.xn, self.Wqkv, self.Wo, self.parts[r], self.batch, self.seq,
                               self.H, self.nh, self.d, r, self.P, int(self.causal), tp.TP_BF16,
                               self.ws, self.ws_bytes, self.stream)
@@ -359,6 +375,11 @@ class BlockShard:
         if self.sequence_parallel:
             for r in range(self.P):
                 self.reduce1_scatter(r)
+            return
+        if self.bf16_partials:
+            tp.tp_partial_reduce_residual_ln_bf16(self.parts, self.n_parts, self.T * self.H,
+                                                  self.X, self.g2, self.b2, self.eps, self.h,
+                                                  self.hn, self.T, self.H, self.stream)
             return
         tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, self.T * self.H, self.X, self.g2,
                                          self.b2, self.eps, self.h, self.hn, self.T, self.H,
@@ -383,6 +404,10 @@ class BlockShard:
             tp.tp_row_linear_fold(self.Yr[r], fl, self.W2, self.parts[0], self.T, self.F, self.H,
                                   r, self.P, int(r > 0), tp.TP_BF16, self.stream)
             return
+        if self.bf16_partials:
+            tp.tp_row_linear_partial_bf16(self.Yr[r], fl, self.W2, self.parts[r], self.T, self.F,
+                                          self.H, r, self.P, self.stream)
+            return
         tp.tp_row_linear_partial(self.Yr[r], fl, self.W2, self.parts[r], self.T, self.F, self.H,
                                  r, self.P, tp.TP_BF16, self.stream)
 
@@ -390,6 +415,11 @@ class BlockShard:
         if self.sequence_parallel:
             for r in range(self.P):
                 self.reduce2_scatter(r)
+            return
+        if self.bf16_partials:
+            tp.tp_partial_reduce_residual_ln_bf16(self.parts, self.n_parts, self.T * self.H,
+                                                  self.h, None, None, 0.0, self.out, None, self.T,
+                                                  self.H, self.stream)
             return
         tp.tp_partial_reduce_residual_ln(self.parts, self.n_parts, self.T * self.H, self.h, None,
                                          None, 0.0, self.out, None, self.T, self.H, tp.TP_BF16,

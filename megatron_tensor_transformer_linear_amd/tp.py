@@ -34,7 +34,8 @@ EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_row_linear_fold",
             "tp_col_linear_gelu_save", "tp_row_linear_backward", "tp_col_linear_backward",
             "tp_attn_workspace_bytes", "tp_attn_head_shard", "tp_attn_head_shard_fold",
             "tp_attn_head_shard_noalloc", "tp_partial_reduce_residual_ln",
-            "tp_partial_reduce_scatter_residual_ln", "tp_status_string")
+            "tp_partial_reduce_scatter_residual_ln", "tp_row_linear_partial_bf16",
+            "tp_attn_head_shard_bf16", "tp_partial_reduce_residual_ln_bf16", "tp_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -76,6 +77,15 @@ lib.tp_partial_reduce_residual_ln.restype = _int
 lib.tp_partial_reduce_scatter_residual_ln.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp,
                                                       _vp, _i64, _i64, _int, _int, _int, _vp]
 lib.tp_partial_reduce_scatter_residual_ln.restype = _int
+lib.tp_row_linear_partial_bf16.argtypes = [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                           _vp]
+lib.tp_row_linear_partial_bf16.restype = _int
+lib.tp_attn_head_shard_bf16.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int,
+                                        _int, _int, _vp, _sz, _vp]
+lib.tp_attn_head_shard_bf16.restype = _int
+lib.tp_partial_reduce_residual_ln_bf16.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp, _vp,
+                                                   _i64, _i64, _vp]
+lib.tp_partial_reduce_residual_ln_bf16.restype = _int
 lib.tp_status_string.argtypes = [_int]
 lib.tp_status_string.restype = ctypes.c_char_p
 
@@ -188,6 +198,32 @@ def tp_attn_head_shard_noalloc(Xn, Wqkv, Wo, Zpart, batch: int, seq: int, H: int
                                                  batch, seq, H, n_heads, head_dim, rank, world,
                                                  int(causal), dtype, _stream(stream)),
                   "tp_attn_head_shard_noalloc")
+
+
+def tp_row_linear_partial_bf16(X, ldx: int, W, Zpart, seq: int, K: int, N: int, rank: int,
+                               world: int, stream=None) -> int:
+    return _check(lib.tp_row_linear_partial_bf16(_ptr(X), ldx, _ptr(W), _ptr(Zpart), seq, K, N,
+                                                 rank, world, _stream(stream)),
+                  "tp_row_linear_partial_bf16")
+
+
+def tp_attn_head_shard_bf16(Xn, Wqkv, Wo, Zpart, batch: int, seq: int, H: int, n_heads: int,
+                            head_dim: int, rank: int, world: int, causal: int, workspace,
+                            workspace_bytes: int, stream=None) -> int:
+    return _check(lib.tp_attn_head_shard_bf16(_ptr(Xn), _ptr(Wqkv), _ptr(Wo), _ptr(Zpart), batch,
+                                              seq, H, n_heads, head_dim, rank, world, int(causal),
+                                              _ptr(workspace), workspace_bytes, _stream(stream)),
+                  "tp_attn_head_shard_bf16")
+
+
+def tp_partial_reduce_residual_ln_bf16(parts, n_parts: int, part_stride: int, residual, gamma,
+                                       beta, eps: float, h_out, y_out, rows: int, H: int,
+                                       stream=None) -> int:
+    return _check(lib.tp_partial_reduce_residual_ln_bf16(_ptr(parts), n_parts, part_stride,
+                                                         _ptr(residual), _ptr(gamma), _ptr(beta),
+                                                         eps, _ptr(h_out), _ptr(y_out), rows, H,
+                                                         _stream(stream)),
+                  "tp_partial_reduce_residual_ln_bf16")
 
 
 def tp_partial_reduce_residual_ln(parts, n_parts: int, part_stride: int, residual, gamma, beta,

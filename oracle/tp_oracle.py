@@ -45,7 +45,8 @@ __all__ = [
     "split_qkv", "head_range", "attention_heads", "attn_head_shard", "mlp_shard",
     "block_shard", "block_forward", "reduce_scatter_rows", "reduce_scatter_residual_layernorm",
     "concat_rows", "gelu_tanh_grad", "row_linear_backward", "col_linear_backward",
-    "mlp_shard_backward", "mlp_backward",
+    "mlp_shard_backward", "mlp_backward", "round_bf16", "row_linear_partial_bf16",
+    "attn_head_shard_bf16",
 ]
 
 F64 = np.float64
@@ -172,6 +173,36 @@ def reduce_partials(parts: Sequence[np.ndarray]) -> np.ndarray:
     for p in parts[1:]:
         acc += _f64(p)
     return acc
+
+
+def round_bf16(x) -> np.ndarray:
+    """x rounded to the nearest bfloat16 value, ties to even, returned in float64.
+
+    bfloat16 keeps float32's exponent range and 8 significant bits: a normal value
+    2^e * 1.f has the quantum 2^(e-7); below the smallest normal 2^-126 the quantum stays
+    2^-133 (subnormals).  The quotient x / quantum is an exact float64 (a power-of-two
+    scaling), so one round-half-to-even of it is the correctly rounded result.  Values whose
+    rounded magnitude exceeds the largest bfloat16 (2 - 2^-7) * 2^127 become infinities."""
+    x = _f64(x)
+    out = np.zeros_like(x)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])                      # x = m * 2^e with 0.5 <= |m| < 1
+    q = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)  # the quantum at x's binade
+    r = np.rint(x[fin] / q) * q
+    big = np.abs(r) > (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r[big] = np.copysign(np.inf, r[big])
+    out[fin] = r
+    out[~fin] = x[~fin]                          # zeros (with their sign), infinities, NaN
+    return out
+
+
+def row_linear_partial_bf16(X, W, rank: int, world: int,
+                            rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Rank r's row-parallel partial as it is exchanged in bf16: row_linear_partial rounded
+    once to bfloat16.  [pwwt] section 5.2 counts the all-reduce's [S, H] input at 2 bytes per
+    element (BF16), and section 6.3 names BF16 arithmetic and the summation order as where
+    tensor-parallel results part from one device's."""
+    return round_bf16(row_linear_partial(X, W, rank, world, rows))
 
 
 def row_linear_fold(Zsum, X, W, rank: int, world: int, accumulate: bool) -> np.ndarray:
@@ -422,6 +453,15 @@ def attn_head_shard(Xn, Wqkv, Wo, n_heads: int, head_dim: int, rank: int, world:
     return matmul(A, Wo[h0 * head_dim: h1 * head_dim, :])
 
 
+def attn_head_shard_bf16(Xn, Wqkv, Wo, n_heads: int, head_dim: int, rank: int, world: int,
+                         batch: int, seq: int, causal: bool = True,
+                         rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Rank r's attention partial exchanged in bf16 (as row_linear_partial_bf16): the
+    output projection's partial rounded once to bfloat16."""
+    return round_bf16(attn_head_shard(Xn, Wqkv, Wo, n_heads, head_dim, rank, world, batch, seq,
+                                      causal, rows))
+
+
 def attn_head_shard_fold(Zsum, Xn, Wqkv, Wo, n_heads: int, head_dim: int, rank: int,
                          world: int, batch: int, seq: int, causal: bool = True,
                          accumulate: bool = True) -> np.ndarray:
@@ -461,7 +501,7 @@ def _needed_rows(rows: np.ndarray, batch: int, seq: int, causal: bool) -> np.nda
 def block_shard(X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, *, n_heads: int,
                 head_dim: int, world: int, batch: int, seq: int, causal: bool = True,
                 eps: float = 1e-5, rows: Optional[Sequence[int]] = None,
-                keep_partials: bool = True) -> Dict[str, object]:
+                keep_partials: bool = True, bf16_partials: bool = False) -> Dict[str, object]:
     """The whole block with every rank's shard, composed as
         Xn = LN(X); h = X + sum_r Attn_r(Xn); hn = LN(h); out = h + sum_r MLP_r(hn)
     ([pwwt] section 2.1 figure 3: LayerNorm, QKV, attention, O, residual add,
@@ -470,6 +510,8 @@ def block_shard(X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, *, n_heads: i
 
     Every step after attention is row-local, so ``rows`` restricts the result to
     those tokens; Xn is computed for the token prefixes their causal keys need.
+    bf16_partials: every rank's partial is rounded once to bfloat16 before the sums
+    (row_linear_partial_bf16).
     Returns a dict with xn, attn_parts (list over ranks), h, hn, mlp_parts, out.
     """
     T, H = X.shape
@@ -481,10 +523,11 @@ def block_shard(X, Wqkv, Wo, W1, W2, gamma1, beta1, gamma2, beta2, *, n_heads: i
         Xn = layer_norm(X, gamma1, beta1, eps)
     else:
         Xn[need] = layer_norm(X[need], gamma1, beta1, eps)
-    attn_parts = [attn_head_shard(Xn, Wqkv, Wo, n_heads, head_dim, r, world, batch, seq,
-                                  causal, rows) for r in range(world)]
+    rnd = round_bf16 if bf16_partials else (lambda a: a)
+    attn_parts = [rnd(attn_head_shard(Xn, Wqkv, Wo, n_heads, head_dim, r, world, batch, seq,
+                                      causal, rows)) for r in range(world)]
     h, hn = reduce_residual_layernorm(attn_parts, X[rows], gamma2, beta2, eps)
-    mlp_parts = [mlp_shard(hn, W1, W2, r, world) for r in range(world)]
+    mlp_parts = [rnd(mlp_shard(hn, W1, W2, r, world)) for r in range(world)]
     out, _ = reduce_residual_layernorm(mlp_parts, h)
     res = {"rows": rows, "xn": Xn[rows], "h": h, "hn": hn, "out": out}
     if keep_partials:

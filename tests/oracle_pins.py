@@ -645,6 +645,71 @@ def pin_mlp_backward_finite_difference():
         assert abs(fd - got) <= 1e-7 * max(1.0, abs(fd)), f"d{name}{idx}: {got} vs {fd}"
 
 
+# ----------------------------------------------------------------------------- bf16 partials
+def pin_round_bf16_closed_forms():
+    """Round to nearest, ties to even, at the points where a mistake shows: exact values,
+    ties in both directions, the carry into the next binade, overflow, subnormals, zeros."""
+    cases = [
+        (1.0, 1.0), (1 + 2 ** -7, 1 + 2 ** -7),           # representable
+        (1 + 2 ** -8, 1.0),                                # tie -> even (down)
+        (1 + 3 * 2 ** -8, 1 + 2 ** -6),                    # tie -> even (up)
+        (1 + 2 ** -8 + 2 ** -20, 1 + 2 ** -7),             # above the tie
+        (-(1 + 2 ** -8), -1.0),                            # sign
+        (2 - 2 ** -9, 2.0),                                # carries into the next binade
+        (257.0, 256.0), (259.0, 260.0), (256.0, 256.0),    # integers: quantum 2 above 256
+        ((2 - 2 ** -7) * 2.0 ** 127, (2 - 2 ** -7) * 2.0 ** 127),  # largest finite
+        ((2 - 2 ** -8) * 2.0 ** 127, math.inf),            # tie above the largest -> inf
+        (2.0 ** -130, 2.0 ** -130),                        # subnormal, representable
+        (1.5 * 2.0 ** -133, 2.0 ** -132),                  # subnormal tie -> even
+        (2.0 ** -134, 0.0),                                # half the smallest -> 0 (even)
+        (0.0, 0.0), (math.inf, math.inf),
+    ]
+    x = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases])
+    got = O.round_bf16(x)
+    assert np.array_equal(got, want), list(zip(x.tolist(), got.tolist(), want.tolist()))
+    assert math.copysign(1.0, O.round_bf16(np.array([-0.0]))[0]) < 0
+
+
+def pin_round_bf16_library():
+    """torch's float32 -> bfloat16 conversion (round to nearest even) on float32 values over
+    the whole exponent range: bit-for-bit the same results."""
+    rng = _rng(900)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-85, 85, 20000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def pin_row_partial_bf16_integers():
+    """Integer partials: exact in bf16 up to 256 in magnitude, rounded to even steps of 2
+    between 256 and 512 -- the rounding is applied to each rank's partial, not to the sum."""
+    rng = _rng(901)
+    X = _ints(rng, (9, 40), -1, 1)
+    W = _ints(rng, (40, 16), -2, 2)
+    for r in range(2):
+        exact = O.row_linear_partial(X, W, r, 2)
+        got = O.row_linear_partial_bf16(X, W, r, 2)
+        assert np.array_equal(got, exact), "small integer partials are exact in bf16"
+    Xb = np.full((1, 4), 64.0)
+    Wb = np.array([[1.0], [1.0], [1.0], [1.0 + 1 / 64]])   # partial of rank 0 of 1: 257
+    assert O.row_linear_partial(Xb, Wb, 0, 1)[0, 0] == 257.0
+    assert O.row_linear_partial_bf16(Xb, Wb, 0, 1)[0, 0] == 256.0
+    blk = O.block_shard(*_block_args(), n_heads=2, head_dim=4, world=2, batch=1, seq=3,
+                        bf16_partials=True)
+    for p in blk["attn_parts"] + blk["mlp_parts"]:
+        assert np.array_equal(p, O.round_bf16(p)), "block partials are bf16 values"
+
+
+def _block_args():
+    rng = _rng(902)
+    H, F = 8, 16
+    X = rng.standard_normal((3, H))
+    g, b = np.ones(H), np.zeros(H)
+    return (X, rng.standard_normal((H, 3 * H)) / 3, rng.standard_normal((H, H)) / 3,
+            rng.standard_normal((H, F)) / 3, rng.standard_normal((F, H)) / 4, g, b, g, b)
+
+
 # ----------------------------------------------------------------------------- accounting
 def pin_byte_accounting_golden():
     vals = {}

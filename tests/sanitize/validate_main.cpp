@@ -56,6 +56,10 @@ int main() {
   expect("reduce H % 8", tp_partial_reduce_residual_ln(F, 2, 64 * 260, P, P, P, 1e-5f, P, P, 64, 260, TP_BF16, nullptr), TP_ERR_ALIGN);
   expect("reduce valid -> launch", tp_partial_reduce_residual_ln(F, 2, 64 * 256, P, P, P, 1e-5f, P, P, 64, 256, TP_BF16, nullptr), TP_ERR_LAUNCH);
   expect("scatter rank", tp_partial_reduce_scatter_residual_ln(F, 2, 64 * 256, P, P, P, 1e-5f, P, P, 64, 256, 4, 4, TP_BF16, nullptr), TP_ERR_RANK);
+  expect("row bf16 valid -> launch", tp_row_linear_partial_bf16(P, 1024, P, P, 64, 1024, 256, 1, 2, nullptr), TP_ERR_LAUNCH);
+  expect("attn bf16 valid -> launch", tp_attn_head_shard_bf16(P, P, P, P, 2, 128, 1024, 8, 128, 0, 2, 1, P, ws, nullptr), TP_ERR_LAUNCH);
+  expect("reduce bf16 stride % 8", tp_partial_reduce_residual_ln_bf16(P, 2, 64 * 256 + 4, P, P, P, 1e-5f, P, P, 64, 256, nullptr), TP_ERR_ALIGN);
+  expect("reduce bf16 valid -> launch", tp_partial_reduce_residual_ln_bf16(P, 2, 64 * 256, P, P, P, 1e-5f, P, P, 64, 256, nullptr), TP_ERR_LAUNCH);
   for (int s = 1; s >= -12; --s) {
     const char* str = tp_status_string(s);
     ++calls;
@@ -78,6 +82,8 @@ int main() {
               valid_status("reduce", tp_partial_reduce_residual_ln(F, r + 1, c, P, P, P, 1e-5f, P, P, a, b, dt, nullptr));
               valid_status("scatter", tp_partial_reduce_scatter_residual_ln(F, r + 1, c, P, P, P, 1e-5f, P, P, a, b, r, w, dt, nullptr));
             }
+            valid_status("row bf16", tp_row_linear_partial_bf16(P, b, P, P, a, b, c, r, w, nullptr));
+            valid_status("reduce bf16", tp_partial_reduce_residual_ln_bf16(P, r + 1, c, P, P, P, 1e-5f, P, P, a, b, nullptr));
           }
   for (int64_t bt : SIZES)
     for (int64_t sq : SIZES)
@@ -91,6 +97,7 @@ int main() {
                 valid_status("attn", tp_attn_head_shard(P, P, P, F, bt, sq, h, nh, hd, r, w, r & 1, TP_BF16, P, need, nullptr));
                 valid_status("attn fold", tp_attn_head_shard_fold(P, P, P, F, bt, sq, h, nh, hd, r, w, 1, r & 1, TP_BF16, P, need, nullptr));
                 valid_status("attn noalloc", tp_attn_head_shard_noalloc(P, P, P, F, bt, sq, h, nh, hd, r, w, 1, TP_BF16, nullptr));
+                valid_status("attn bf16", tp_attn_head_shard_bf16(P, P, P, P, bt, sq, h, nh, hd, r, w, 1, P, need, nullptr));
               }
             }
   std::printf("%ld checks, %d failures\n", calls, failures);

@@ -185,6 +185,31 @@ def colb(tp, **kw):
                                          a["world"], a["acc"], a["dtype"], a["stream"])
 
 
+def rowh(tp, **kw):
+    a = dict(X=P, ldx=1024, W=P, Z=P, seq=64, K=1024, N=256, rank=1, world=2, stream=None)
+    a.update(kw)
+    return tp.lib.tp_row_linear_partial_bf16(a["X"], a["ldx"], a["W"], a["Z"], a["seq"], a["K"],
+                                             a["N"], a["rank"], a["world"], a["stream"])
+
+
+def attnh(tp, **kw):
+    a = dict(Xn=P, Wqkv=P, Wo=P, Z=P, batch=2, seq=64, H=1024, nh=8, d=128, rank=0, world=4,
+             causal=1, ws=P, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return tp.lib.tp_attn_head_shard_bf16(a["Xn"], a["Wqkv"], a["Wo"], a["Z"], a["batch"],
+                                          a["seq"], a["H"], a["nh"], a["d"], a["rank"],
+                                          a["world"], a["causal"], a["ws"], a["wsb"], a["stream"])
+
+
+def redh(tp, **kw):
+    a = dict(parts=P, n=4, stride=64 * 256, res=P, g=P, b=P, eps=1e-5, h=P, y=P, rows=64, H=256,
+             stream=None)
+    a.update(kw)
+    return tp.lib.tp_partial_reduce_residual_ln_bf16(a["parts"], a["n"], a["stride"], a["res"],
+                                                     a["g"], a["b"], a["eps"], a["h"], a["y"],
+                                                     a["rows"], a["H"], a["stream"])
+
+
 CASES = [
     # column-parallel linear
     ("col null X", col, dict(X=None), "TP_ERR_NULL"),
@@ -234,6 +259,32 @@ CASES = [
     ("fold N % 8", rowf, dict(N=252), "TP_ERR_ALIGN"),
     ("fold ldx beyond 2^21", rowf, dict(ldx=(1 << 21) + 8), "TP_ERR_SHAPE"),
     ("fold first rank null Z", rowf, dict(Z=None, acc=0, rank=0), "TP_ERR_NULL"),
+    # row-parallel partial in bf16
+    ("row bf16 null X", rowh, dict(X=None), "TP_ERR_NULL"),
+    ("row bf16 null Z", rowh, dict(Z=None), "TP_ERR_NULL"),
+    ("row bf16 rank = world", rowh, dict(rank=2), "TP_ERR_RANK"),
+    ("row bf16 ldx < K/world", rowh, dict(ldx=504), "TP_ERR_SHAPE"),
+    ("row bf16 K % world", rowh, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("row bf16 misaligned Z", rowh, dict(Z=P + 8), "TP_ERR_ALIGN"),
+    ("row bf16 N % 8", rowh, dict(N=252), "TP_ERR_ALIGN"),
+    # attention-head shard with a bf16 partial
+    ("attn bf16 null Z", attnh, dict(Z=None), "TP_ERR_NULL"),
+    ("attn bf16 bad rank", attnh, dict(rank=4), "TP_ERR_RANK"),
+    ("attn bf16 H != heads*d", attnh, dict(H=1000), "TP_ERR_SHAPE"),
+    ("attn bf16 heads % world", attnh, dict(world=3, rank=0), "TP_ERR_DIVISIBLE"),
+    ("attn bf16 small workspace", attnh, dict(wsb=1000), "TP_ERR_WORKSPACE"),
+    ("attn bf16 misaligned Z", attnh, dict(Z=P + 8), "TP_ERR_ALIGN"),
+    # reduce + residual + LN over bf16 partials
+    ("reduce bf16 negative parts", redh, dict(n=-1), "TP_ERR_SHAPE"),
+    ("reduce bf16 null parts", redh, dict(parts=None), "TP_ERR_NULL"),
+    ("reduce bf16 nothing to read", redh, dict(n=0, parts=None, res=None), "TP_ERR_NULL"),
+    ("reduce bf16 gamma without y", redh, dict(y=None), "TP_ERR_NULL"),
+    ("reduce bf16 rows 0", redh, dict(rows=0), "TP_ERR_SHAPE"),
+    ("reduce bf16 NaN eps", redh, dict(eps=float("nan")), "TP_ERR_SHAPE"),
+    ("reduce bf16 stride too small", redh, dict(stride=64 * 256 - 8), "TP_ERR_SHAPE"),
+    ("reduce bf16 stride % 8", redh, dict(stride=64 * 256 + 4), "TP_ERR_ALIGN"),
+    ("reduce bf16 H % 8", redh, dict(H=252, stride=64 * 252), "TP_ERR_ALIGN"),
+    ("reduce bf16 misaligned parts", redh, dict(parts=P + 8), "TP_ERR_ALIGN"),
     # attention-head shard
     ("attn null Wo", attn, dict(Wo=None), "TP_ERR_NULL"),
     ("attn f32", attn, dict(dtype=0), "TP_ERR_DTYPE"),

@@ -203,7 +203,45 @@ def _attn_fold_ignores_running_sum(Zsum, *args, accumulate=True, **kw):
     return _orig["attn_head_shard_fold"](Zsum, *args, accumulate=False, **kw)
 
 
+def _bf16_half_away(x):
+    x = np.asarray(x, np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    q = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    out[fin] = np.sign(x[fin]) * np.floor(np.abs(x[fin]) / q + 0.5) * q
+    return out
+
+
+def _bf16_truncate(x):
+    x = np.asarray(x, np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    q = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    out[fin] = np.trunc(x[fin] / q) * q
+    return out
+
+
+def _bf16_seven_bits(x):
+    x = np.asarray(x, np.float64)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    q = np.ldexp(1.0, np.maximum(e - 1, -126) - 6)
+    out[fin] = np.rint(x[fin] / q) * q
+    return out
+
+
+def _row_partial_bf16_unrounded(X, W, rank, world, rows=None):
+    return _orig["row_linear_partial"](X, W, rank, world, rows)
+
+
 MUTATIONS = {
+    "bf16_round_half_away": ("round_bf16", _bf16_half_away),
+    "bf16_truncate": ("round_bf16", _bf16_truncate),
+    "bf16_seven_significant_bits": ("round_bf16", _bf16_seven_bits),
+    "row_partial_bf16_unrounded": ("row_linear_partial_bf16", _row_partial_bf16_unrounded),
     "shard_off_by_one": ("shard_range", _shard_off_by_one),
     "shard_reversed_ranks": ("shard_range", _shard_reversed),
     "shard_floor_remainder": ("shard_range", _shard_floor),

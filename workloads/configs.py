@@ -139,10 +139,10 @@ def tensor_bytes(rows: int, cols: int, dtype: str) -> int:
 
 
 def reduce_bytes(rows: int, hidden: int, n_parts: int, dtype: str, residual: bool,
-                 h_out: bool, y_out: bool) -> int:
-    """Algorithmic HBM bytes of one reduce + residual + LayerNorm pass: every fp32
-    partial and the residual read once, every output written once (gamma and beta,
-    a single row each, are not counted)."""
-    b = n_parts * tensor_bytes(rows, hidden, "f32")
+                 h_out: bool, y_out: bool, parts_dtype: str = "f32") -> int:
+    """Algorithmic HBM bytes of one reduce + residual + LayerNorm pass: every partial
+    (fp32, or bf16 for the bf16-partial variant) and the residual read once, every output
+    written once (gamma and beta, a single row each, are not counted)."""
+    b = n_parts * tensor_bytes(rows, hidden, parts_dtype)
     b += (int(residual) + int(h_out) + int(y_out)) * tensor_bytes(rows, hidden, dtype)
     return b
