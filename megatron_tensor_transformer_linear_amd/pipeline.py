@@ -68,8 +68,7 @@ class MLPShard:
         self.Yfull = torch.empty(self.T, self.F, dtype=torch_dtype(dtype), device=dev)
         # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
         self.n_parts = 1 if fold else world
-        self.parts = torch.empty(self.n_parts, self.T, self.H,
-                                 dtype=bf if bf16_partials else torch.float32, device=dev)
+        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
         if residual_ln:
             self.h = torch.empty(self.T, self.H, dtype=torch_dtype(dtype), device=dev)
             self.y = torch.empty_like(self.h)
@@ -257,8 +256,7 @@ class AttnShard:
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         # The ranks' fp32 partials, stacked [P, T, H]; with fold, one running sum [1, T, H].
         self.n_parts = 1 if fold else world
-        self.parts = torch.empty(self.n_parts, self.T, self.H,
-                                 dtype=bf if bf16_partials else torch.float32, device=dev)
+        self.parts = torch.empty(self.n_parts, self.T, self.H, dtype=torch.float32, device=dev)
         self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
 
     def workspace_views(self):
