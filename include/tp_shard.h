@@ -6,13 +6,14 @@
  * (by pointing each rank's output at its column block); where it places an all-reduce,
  * the ranks' fp32 partials are stacked in HBM and summed by
  * tp_partial_reduce_residual_ln, fused with the residual add and LayerNorm, or summed in
- * place by the producing product's epilogue (the *_fold calls).
+ * place by the producing product's epilogue (the *_fold calls), or stored in bf16 and summed
+ * by tp_partial_reduce_residual_ln_bf16 (the *_bf16 calls).
  *
  * Sources (web pages on tensor parallelism):
  *   typc.net "张量并行：千亿大模型突破单卡显存限制的底层技术", sections 2.1, 2.2, 3;
  *   0539edu.com TP / 3D-parallelism tutorial, sections 1.1 and 1.2 (formulas 1.1-1.13);
  *   pwwt.cn TP layout walk-through, sections 1.1-1.2 (figures 1-2), 2.1-2.3 (figures 3-5),
- *   3.1-3.4 (the weight-chunk helper and the column/row parallel layers), 5.3 and 6.3.
+ *   3.1-3.4 (the weight-chunk helper and the column/row parallel layers), 5.1-5.3 and 6.3.
  *
  * Conventions shared by every call
  *   - A linear layer is Y = X.W with X [seq, H] and W [H, N] (pwwt.cn section 1.1); every
