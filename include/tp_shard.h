@@ -340,6 +340,18 @@ int tp_partial_reduce_scatter_residual_ln(const float* parts, int n_parts, int64
                                           int64_t rows, int64_t H, int rank, int world, int dtype,
                                           void* stream);
 
+/* The sequence-parallel epilogue over bf16 partials: tp_partial_reduce_scatter_residual_ln's
+ * rows of rank `rank`, with the partials, the residual and the outputs in bf16 as for
+ * tp_partial_reduce_residual_ln_bf16 (part_stride a multiple of 8 when n_parts > 1).  Each
+ * output row is computed by the same arithmetic as the corresponding row of
+ * tp_partial_reduce_residual_ln_bf16.  Errors: as tp_partial_reduce_residual_ln_bf16, plus
+ * TP_ERR_RANK and TP_ERR_DIVISIBLE (rows % world). */
+int tp_partial_reduce_scatter_residual_ln_bf16(const void* parts, int n_parts,
+                                               int64_t part_stride, const void* residual,
+                                               const void* gamma, const void* beta, float eps,
+                                               void* h_out, void* y_out, int64_t rows, int64_t H,
+                                               int rank, int world, void* stream);
+
 /* Static, NUL-terminated description of a tp_status value. */
 const char* tp_status_string(int status);
 

@@ -596,4 +596,46 @@ int tp_partial_reduce_scatter_residual_ln(const float* parts, int n_parts, int64
   return launched(launch_reduce_ln(r, (hipStream_t)stream));
 }
 
+int tp_partial_reduce_scatter_residual_ln_bf16(const void* parts, int n_parts,
+                                               int64_t part_stride, const void* residual,
+                                               const void* gamma, const void* beta, float eps,
+                                               void* h_out, void* y_out, int64_t rows, int64_t H,
+                                               int rank, int world, void* stream) {
+  if (int st = check_rank(rank, world)) return st;
+  if (n_parts < 0) return TP_ERR_SHAPE;
+  if (n_parts > 0 && !parts) return TP_ERR_NULL;
+  if (n_parts == 0 && !residual) return TP_ERR_NULL;
+  if (gamma && !y_out) return TP_ERR_NULL;
+  if (!gamma && !h_out) return TP_ERR_NULL;
+  if (rows <= 0 || rows > INT32_MAX || H <= 0 || H > 65536) return TP_ERR_SHAPE;
+  if (rows % world) return TP_ERR_DIVISIBLE;
+  if (!(eps >= 0.0f) || isinf(eps)) return TP_ERR_SHAPE;
+  if (n_parts > 1 && part_stride < rows * H) return TP_ERR_SHAPE;
+  if (!mult8(H)) return TP_ERR_ALIGN;
+  if (n_parts > 1 && !mult8(part_stride)) return TP_ERR_ALIGN;
+  const void* ptrs[] = {parts, residual, gamma, beta, h_out, y_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return TP_ERR_ALIGN;
+
+  // Rows [rank*rows/world, (rank+1)*rows/world) of every bf16 partial and of the residual.
+  const int64_t rl = rows / world, row0 = (int64_t)rank * rl;
+  const size_t off = (size_t)(row0 * H) * 2;
+  ReduceDesc r;
+  r.parts = parts ? (const float*)((const char*)parts + off) : nullptr;  // read as bf16
+  r.n_parts = n_parts;
+  r.part_stride = part_stride;
+  r.residual = residual ? (const char*)residual + off : nullptr;
+  r.gamma = gamma;
+  r.beta = beta;
+  r.eps = eps;
+  r.h_out = h_out;
+  r.y_out = gamma ? y_out : nullptr;
+  r.rows = rl;
+  r.H = H;
+  r.bf16 = 1;
+  r.parts_bf16 = 1;
+  (void)hipGetLastError();
+  return launched(launch_reduce_ln(r, (hipStream_t)stream));
+}
+
 }  // extern "C"

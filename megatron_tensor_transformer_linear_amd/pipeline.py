@@ -321,8 +321,8 @@ class BlockShard:
         self.sequence_parallel = sequence_parallel
         self.fold = fold
         self.bf16_partials = bf16_partials
-        if bf16_partials and (fold or sequence_parallel):
-            raise ValueError("bf16 partials are built for the stacked epilogue only")
+        if bf16_partials and fold:
+            raise ValueError("the fold keeps one fp32 running sum: no bf16 partials")
         if sequence_parallel and self.T % world:
             raise ValueError("sequence parallelism needs tokens divisible by the world size")
         dev = X.device
@@ -386,6 +386,13 @@ class BlockShard:
     def reduce1_scatter(self, r: int):
         """Rank r's reduce-scatter + residual + LN2 into its rows of h and hn."""
         a, n = self._scatter_rows(r)
+        if self.bf16_partials:
+            tp.tp_partial_reduce_scatter_residual_ln_bf16(self.parts, self.n_parts,
+                                                          self.T * self.H, self.X, self.g2,
+                                                          self.b2, self.eps, self.h[a:a + n],
+                                                          self.hn[a:a + n], self.T, self.H, r,
+                                                          self.P, self.stream)
+            return
         tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.n_parts, self.T * self.H, self.X,
                                                  self.g2, self.b2, self.eps, self.h[a:a + n],
                                                  self.hn[a:a + n], self.T, self.H, r, self.P,
@@ -426,6 +433,12 @@ class BlockShard:
     def reduce2_scatter(self, r: int):
         """Rank r's reduce-scatter + residual into its rows of out."""
         a, n = self._scatter_rows(r)
+        if self.bf16_partials:
+            tp.tp_partial_reduce_scatter_residual_ln_bf16(self.parts, self.n_parts,
+                                                          self.T * self.H, self.h, None, None,
+                                                          0.0, self.out[a:a + n], None, self.T,
+                                                          self.H, r, self.P, self.stream)
+            return
         tp.tp_partial_reduce_scatter_residual_ln(self.parts, self.n_parts, self.T * self.H, self.h,
                                                  None, None, 0.0, self.out[a:a + n], None,
                                                  self.T, self.H, r, self.P, tp.TP_BF16,

@@ -35,7 +35,8 @@ EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_row_linear_fold",
             "tp_attn_workspace_bytes", "tp_attn_head_shard", "tp_attn_head_shard_fold",
             "tp_attn_head_shard_noalloc", "tp_partial_reduce_residual_ln",
             "tp_partial_reduce_scatter_residual_ln", "tp_row_linear_partial_bf16",
-            "tp_attn_head_shard_bf16", "tp_partial_reduce_residual_ln_bf16", "tp_status_string")
+            "tp_attn_head_shard_bf16", "tp_partial_reduce_residual_ln_bf16",
+            "tp_partial_reduce_scatter_residual_ln_bf16", "tp_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -86,6 +87,9 @@ lib.tp_attn_head_shard_bf16.restype = _int
 lib.tp_partial_reduce_residual_ln_bf16.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32, _vp, _vp,
                                                    _i64, _i64, _vp]
 lib.tp_partial_reduce_residual_ln_bf16.restype = _int
+lib.tp_partial_reduce_scatter_residual_ln_bf16.argtypes = [_vp, _int, _i64, _vp, _vp, _vp, _f32,
+                                                           _vp, _vp, _i64, _i64, _int, _int, _vp]
+lib.tp_partial_reduce_scatter_residual_ln_bf16.restype = _int
 lib.tp_status_string.argtypes = [_int]
 lib.tp_status_string.restype = ctypes.c_char_p
 
@@ -224,6 +228,16 @@ def tp_partial_reduce_residual_ln_bf16(parts, n_parts: int, part_stride: int, re
                                                          eps, _ptr(h_out), _ptr(y_out), rows, H,
                                                          _stream(stream)),
                   "tp_partial_reduce_residual_ln_bf16")
+
+
+def tp_partial_reduce_scatter_residual_ln_bf16(parts, n_parts: int, part_stride: int, residual,
+                                               gamma, beta, eps: float, h_out, y_out, rows: int,
+                                               H: int, rank: int, world: int,
+                                               stream=None) -> int:
+    return _check(lib.tp_partial_reduce_scatter_residual_ln_bf16(
+        _ptr(parts), n_parts, part_stride, _ptr(residual), _ptr(gamma), _ptr(beta), eps,
+        _ptr(h_out), _ptr(y_out), rows, H, rank, world, _stream(stream)),
+        "tp_partial_reduce_scatter_residual_ln_bf16")
 
 
 def tp_partial_reduce_residual_ln(parts, n_parts: int, part_stride: int, residual, gamma, beta,

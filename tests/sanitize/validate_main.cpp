@@ -84,6 +84,7 @@ int main() {
             }
             valid_status("row bf16", tp_row_linear_partial_bf16(P, b, P, P, a, b, c, r, w, nullptr));
             valid_status("reduce bf16", tp_partial_reduce_residual_ln_bf16(P, r + 1, c, P, P, P, 1e-5f, P, P, a, b, nullptr));
+            valid_status("scatter bf16", tp_partial_reduce_scatter_residual_ln_bf16(P, r + 1, c, P, P, P, 1e-5f, P, P, a, b, r, w, nullptr));
           }
   for (int64_t bt : SIZES)
     for (int64_t sq : SIZES)

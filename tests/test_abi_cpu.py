@@ -210,6 +210,15 @@ def redh(tp, **kw):
                                                      a["rows"], a["H"], a["stream"])
 
 
+def rsh(tp, **kw):
+    a = dict(parts=P, n=4, stride=64 * 256, res=P, g=P, b=P, eps=1e-5, h=P, y=P, rows=64, H=256,
+             rank=1, world=4, stream=None)
+    a.update(kw)
+    return tp.lib.tp_partial_reduce_scatter_residual_ln_bf16(
+        a["parts"], a["n"], a["stride"], a["res"], a["g"], a["b"], a["eps"], a["h"], a["y"],
+        a["rows"], a["H"], a["rank"], a["world"], a["stream"])
+
+
 CASES = [
     # column-parallel linear
     ("col null X", col, dict(X=None), "TP_ERR_NULL"),
@@ -285,6 +294,14 @@ CASES = [
     ("reduce bf16 stride % 8", redh, dict(stride=64 * 256 + 4), "TP_ERR_ALIGN"),
     ("reduce bf16 H % 8", redh, dict(H=252, stride=64 * 252), "TP_ERR_ALIGN"),
     ("reduce bf16 misaligned parts", redh, dict(parts=P + 8), "TP_ERR_ALIGN"),
+    # reduce-scatter over bf16 partials
+    ("scatter bf16 rows % world", rsh, dict(rows=66, stride=66 * 256), "TP_ERR_DIVISIBLE"),
+    ("scatter bf16 rank = world", rsh, dict(rank=4), "TP_ERR_RANK"),
+    ("scatter bf16 null parts", rsh, dict(parts=None), "TP_ERR_NULL"),
+    ("scatter bf16 gamma without y", rsh, dict(y=None), "TP_ERR_NULL"),
+    ("scatter bf16 stride too small", rsh, dict(stride=64 * 256 - 8), "TP_ERR_SHAPE"),
+    ("scatter bf16 stride % 8", rsh, dict(stride=64 * 256 + 4), "TP_ERR_ALIGN"),
+    ("scatter bf16 misaligned h", rsh, dict(h=P + 4), "TP_ERR_ALIGN"),
     # attention-head shard
     ("attn null Wo", attn, dict(Wo=None), "TP_ERR_NULL"),
     ("attn f32", attn, dict(dtype=0), "TP_ERR_DTYPE"),

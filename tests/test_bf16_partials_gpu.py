@@ -87,6 +87,34 @@ def test_reduce_bf16_partials(lib, rows, H, n_parts, residual, ln):
         check("y", y, yref, "bf16")
 
 
+@pytest.mark.parametrize("rows,H,world", [(1024, 12288, 8), (96, 264, 4)])
+def test_reduce_scatter_bf16_partials(lib, rows, H, world):
+    """Every rank's reduce-scatter of bf16 partials writes exactly the rows of the full reduce
+    (same arithmetic per row, bit for bit), and those rows match the oracle."""
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(1400 + rows))
+    n = 8
+    parts = dev_values(rng.standard_normal((n, rows, H)), "bf16")
+    R = dev_values(rng.standard_normal((rows, H)), "bf16")
+    g = dev_values(1 + 0.1 * rng.standard_normal(H), "bf16")
+    b = dev_values(0.1 * rng.standard_normal(H), "bf16")
+    h = torch.empty(rows, H, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty_like(h)
+    hs, ys = torch.full_like(h, 7.0), torch.full_like(h, 7.0)
+    say(f"  bf16-partial reduce-scatter rows={rows} H={H} world={world}")
+    tp.tp_partial_reduce_residual_ln_bf16(parts, n, rows * H, R, g, b, 1e-5, h, y, rows, H)
+    rl = rows // world
+    for r in range(world):
+        tp.tp_partial_reduce_scatter_residual_ln_bf16(parts, n, rows * H, R, g, b, 1e-5,
+                                                      hs[r * rl:], ys[r * rl:], rows, H, r, world)
+    _sync()
+    assert torch.equal(hs.view(torch.int16), h.view(torch.int16)), "h rows differ"
+    assert torch.equal(ys.view(torch.int16), y.view(torch.int16)), "y rows differ"
+    href, yref = O.reduce_residual_layernorm(list(host(parts)), host(R), host(g), host(b), 1e-5)
+    check("h", hs, href, "bf16")
+    check("y", ys, yref, "bf16")
+
+
 def test_attn_shard_bf16_partial_is_the_rounded_fp32_partial(lib):
     """Same inputs through tp_attn_head_shard (fp32 partial) and tp_attn_head_shard_bf16: the
     bf16 partial is the fp32 one rounded to nearest even, element for element (one
@@ -161,6 +189,26 @@ def test_small_block_bf16_partials(lib):
         for r in range(cfg.world):
             check(f"attention partial {r} (bf16)", sh.parts[r], ref["attn_parts"][r], "bf16")
     _check_block(sh, cfg, t, attn_checks)
+
+
+def test_block_sequence_parallel_bf16_partials(lib):
+    """The block with bf16 partials and sequence-parallel epilogues (every rank's
+    reduce-scatter of its rows, written at their offsets) is bit-identical to the stacked
+    epilogues."""
+    tp, pl = lib
+    cfg = small_variant("block_bf16_tp8")
+    t = generate(cfg)
+    a = _block(pl, cfg, t)
+    args = (dev(t["X"]), dev_values(_qkv_values(t), "bf16"), dev(t["Wo"]), dev(t["W1"]),
+            dev(t["W2"]), dev(t["gamma"]), dev(t["beta"]), dev(t["gamma"]), dev(t["beta"]),
+            cfg.world, cfg.batch, cfg.seq, cfg.n_heads, cfg.head_dim, cfg.causal, cfg.eps)
+    b = pl.BlockShard(*args, sequence_parallel=True, bf16_partials=True)
+    say(f"  small block, bf16 partials, stacked and sequence-parallel epilogues {cfg}")
+    a.step()
+    b.step()
+    _sync()
+    for name in ("xn", "h", "hn", "out"):
+        assert torch.equal(getattr(a, name).view(torch.int16), getattr(b, name).view(torch.int16)), name
 
 
 @pytest.mark.timeout(600)
