@@ -28,8 +28,8 @@ rank's reduce-scatter of its 1024 rows) and the backward pass of the MLP pair (t
 gradient products of every rank and the reduce of the input-gradient partials; --no-backward
 skips it) are timed on their own and reported beside the step, outside `value`, and so is the
 same step with each epilogue's reduce folded into the row-parallel products (one fp32 running
-sum instead of 8 stacked partials) and with the 8 partials stored in bf16 (--no-fold skips
-both).  The other workloads of the path (the
+sum instead of 8 stacked partials; --no-fold skips it) and with the 8 partials stored in bf16
+(--no-bf16-partials skips it).  The other workloads of the path (the
 fp32 MLP, the single linear, the bf16 MLP shard and the attention-head shard) are timed the
 same way and reported per rank under `other_workloads` (--no-workloads skips them).
 """
@@ -674,8 +674,9 @@ def main() -> int:
                     help="skip the measurement of the other workloads (fp32 MLP, single linear, "
                          "bf16 MLP shard, attention-head shard)")
     ap.add_argument("--no-fold", action="store_true",
-                    help="skip the measurements of the step with folded reduces and with "
-                         "bf16 partials")
+                    help="skip the measurement of the step with folded reduces")
+    ap.add_argument("--no-bf16-partials", action="store_true",
+                    help="skip the measurement of the step with bf16 partials")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache pass (each stage after a 512 MiB scratch read)")
     ap.add_argument("--no-clock", action="store_true",
@@ -882,6 +883,7 @@ def main() -> int:
     if not args.no_fold:
         log("timing the block step with folded reduces")
         result["folded_step"] = folded_block_leg(cfg, blk, stream, max(1, min(args.steps, 5)))
+    if not args.no_bf16_partials:
         log("timing the block step with bf16 partials")
         result["bf16_partials_step"] = folded_block_leg(cfg, blk, stream,
                                                         max(1, min(args.steps, 5)), "bf16")
