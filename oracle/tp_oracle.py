@@ -46,7 +46,7 @@ __all__ = [
     "block_shard", "block_forward", "reduce_scatter_rows", "reduce_scatter_residual_layernorm",
     "concat_rows", "gelu_tanh_grad", "row_linear_backward", "col_linear_backward",
     "mlp_shard_backward", "mlp_backward", "round_bf16", "row_linear_partial_bf16",
-    "attn_head_shard_bf16",
+    "attn_head_shard_bf16", "col_linear_backward_bf16",
 ]
 
 F64 = np.float64
@@ -269,23 +269,36 @@ def col_linear_backward(dU, X, W, rank: int, world: int) -> Tuple[np.ndarray, np
     return matmul(dU, _f64(W)[:, n0:n1].T), matmul(X.T, dU)
 
 
-def mlp_shard_backward(X, A, B, dZ, rank: int, world: int, act: str = "gelu_tanh") -> Dict:
+def col_linear_backward_bf16(dU, X, W, rank: int, world: int) -> Tuple[np.ndarray, np.ndarray]:
+    """col_linear_backward with the input-gradient partial exchanged in bf16: dX_part_r
+    rounded once to bfloat16, dW_r unchanged.  The backward all-reduce carries an [S, H]
+    operand like the forward one, which [pwwt] section 5.2 counts at 2 bytes per element."""
+    dX_part, dW = col_linear_backward(dU, X, W, rank, world)
+    return round_bf16(dX_part), dW
+
+
+def mlp_shard_backward(X, A, B, dZ, rank: int, world: int, act: str = "gelu_tanh",
+                       bf16_dx_partials: bool = False) -> Dict:
     """Rank r's backward of mlp_shard: forward U_r = X . A[:, block r], Y_r = act(U_r), then
-    the row layer's backward (fused with act') and the column layer's backward.  Returns
-    {"U", "Y", "dU", "dB", "dA", "dX_part"}: dB is the gradient of B[block r, :], dA of
-    A[:, block r], dX_part the rank's partial of the input gradient."""
+    the row layer's backward (fused with act') and the column layer's backward
+    (col_linear_backward_bf16 when bf16_dx_partials).  Returns {"U", "Y", "dU", "dB", "dA",
+    "dX_part"}: dB is the gradient of B[block r, :], dA of A[:, block r], dX_part the rank's
+    partial of the input gradient."""
     U = col_linear(X, A, rank, world, "none")
     Y = _act(U, act)
     dU, dB = row_linear_backward(dZ, Y, B, rank, world, U, act)
-    dX_part, dA = col_linear_backward(dU, X, A, rank, world)
+    col_bwd = col_linear_backward_bf16 if bf16_dx_partials else col_linear_backward
+    dX_part, dA = col_bwd(dU, X, A, rank, world)
     return {"U": U, "Y": Y, "dU": dU, "dB": dB, "dA": dA, "dX_part": dX_part}
 
 
-def mlp_backward(X, A, B, dZ, world: int, act: str = "gelu_tanh") -> Dict:
+def mlp_backward(X, A, B, dZ, world: int, act: str = "gelu_tanh",
+                 bf16_dx_partials: bool = False) -> Dict:
     """Backward of the whole tensor-parallel MLP: every rank's mlp_shard_backward, then
     dX = sum of the partials (ascending ranks), dA = the column blocks concatenated, dB = the
     row blocks stacked, in rank order.  Returns {"dX", "dA", "dB"}."""
-    shards = [mlp_shard_backward(X, A, B, dZ, r, world, act) for r in range(world)]
+    shards = [mlp_shard_backward(X, A, B, dZ, r, world, act, bf16_dx_partials)
+              for r in range(world)]
     return {"dX": reduce_partials([s["dX_part"] for s in shards]),
             "dA": concat_columns([s["dA"] for s in shards]),
             "dB": concat_rows([s["dB"] for s in shards])}

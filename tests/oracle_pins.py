@@ -701,6 +701,36 @@ def pin_row_partial_bf16_integers():
         assert np.array_equal(p, O.round_bf16(p)), "block partials are bf16 values"
 
 
+def pin_col_backward_bf16_partial():
+    """The bf16 input-gradient partial rounds each rank's dU . W_r^T to nearest, ties to even
+    (257 -> 256 and 259 -> 260, the two neighbours of a tie in the binade [256, 512)), and
+    leaves the weight gradient in full precision."""
+    dU = np.ones((1, 3))
+    W = np.zeros((2, 6))
+    W[0, 3:] = [128.0, 128.0, 1.0]                       # rank 1 of 2: dX_part[0, 0] = 257
+    W[1, 3:] = [128.0, 130.0, 1.0]                       #              dX_part[0, 1] = 259
+    X = np.array([[0.5, 1.0 + 2.0 ** -12]])
+    dXp, dW = O.col_linear_backward(dU, X, W, 1, 2)
+    assert dXp.tolist() == [[257.0, 259.0]]
+    dXh, dWh = O.col_linear_backward_bf16(dU, X, W, 1, 2)
+    assert dXh.tolist() == [[256.0, 260.0]]
+    assert np.array_equal(dWh, dW) and dW[1, 0] == 1.0 + 2.0 ** -12, "dW is not rounded"
+    rng = _rng(903)
+    X, A, B = rng.standard_normal((5, 8)), rng.standard_normal((8, 16)), rng.standard_normal((16, 8))
+    dZ = rng.standard_normal((5, 8))
+    full = O.mlp_backward(X, A, B, dZ, 2)
+    half = O.mlp_backward(X, A, B, dZ, 2, bf16_dx_partials=True)
+    parts = [O.mlp_shard_backward(X, A, B, dZ, r, 2, bf16_dx_partials=True)["dX_part"]
+             for r in range(2)]
+    assert np.array_equal(half["dX"], parts[0] + parts[1])
+    assert np.array_equal(half["dA"], full["dA"]) and np.array_equal(half["dB"], full["dB"])
+    # two partials, each within 2^-8 (half a bf16 quantum) of its own magnitude
+    bound = 2.0 ** -8 * sum(np.abs(O.mlp_shard_backward(X, A, B, dZ, r, 2)["dX_part"])
+                            for r in range(2))
+    assert np.all(np.abs(half["dX"] - full["dX"]) <= bound)
+    assert not np.array_equal(half["dX"], full["dX"])
+
+
 def _block_args():
     rng = _rng(902)
     H, F = 8, 16

@@ -237,11 +237,23 @@ def _row_partial_bf16_unrounded(X, W, rank, world, rows=None):
     return _orig["row_linear_partial"](X, W, rank, world, rows)
 
 
+def _col_bwd_bf16_unrounded(dU, X, W, rank, world):
+    return _orig["col_linear_backward"](dU, X, W, rank, world)
+
+
+def _col_bwd_bf16_rounds_weight_grad(dU, X, W, rank, world):
+    dXp, dW = _orig["col_linear_backward"](dU, X, W, rank, world)
+    return _orig["round_bf16"](dXp), _orig["round_bf16"](dW)
+
+
 MUTATIONS = {
     "bf16_round_half_away": ("round_bf16", _bf16_half_away),
     "bf16_truncate": ("round_bf16", _bf16_truncate),
     "bf16_seven_significant_bits": ("round_bf16", _bf16_seven_bits),
     "row_partial_bf16_unrounded": ("row_linear_partial_bf16", _row_partial_bf16_unrounded),
+    "col_bwd_bf16_unrounded": ("col_linear_backward_bf16", _col_bwd_bf16_unrounded),
+    "col_bwd_bf16_rounds_weight_grad": ("col_linear_backward_bf16",
+                                        _col_bwd_bf16_rounds_weight_grad),
     "shard_off_by_one": ("shard_range", _shard_off_by_one),
     "shard_reversed_ranks": ("shard_range", _shard_reversed),
     "shard_floor_remainder": ("shard_range", _shard_floor),
