@@ -25,8 +25,8 @@ it, so nothing it reads is cached (`stages[*].cold_*`).  The CPU baseline times 
 oracle on a bounded row sample of the same workload on this host, and the full oracle of each
 other workload.  After the timed steps, the sequence-parallel form of the epilogue (each
 rank's reduce-scatter of its 1024 rows) and the backward pass of the MLP pair (the four
-gradient products of every rank and the reduce of the input-gradient partials; --no-backward
-skips it) are timed on their own and reported beside the step, outside `value`, and so is the
+gradient products of every rank and the reduce of the input-gradient partials, with those
+partials also stored in bf16 and reduced; --no-backward skips it) are timed on their own and reported beside the step, outside `value`, and so is the
 same step with each epilogue's reduce folded into the row-parallel products (one fp32 running
 sum instead of 8 stacked partials; --no-fold skips it) and with the 8 partials stored in bf16
 (--no-bf16-partials skips it).  The other workloads of the path (the
@@ -240,7 +240,8 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
     dW1_r = X^T.dU_r, then the reduce of the 8 input-gradient partials.  One untimed pass,
     then two timed passes; each kind of product runs for the 8 ranks back to back and is timed
     as a group with HIP events on its stream at the group boundaries (per launch: the group's
-    time over 8)."""
+    time over 8).  After each pass, the dX partials stored in bf16 and their reduce are timed
+    the same way; pass_bf16_dx_ms is the pass with those two groups swapped in."""
     import torch
     from megatron_tensor_transformer_linear_amd import pipeline as pl
     from workloads import output_gradient
@@ -249,11 +250,14 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
     dZ = pl.to_device(output_gradient(cfg).data, "bf16", dev)
     trn = pl.MLPTrainShard(blk.X, blk.W1, blk.W2, dZ, cfg.world)
     trn.forward()  # saves U_r and Y_r of every rank
+    # The same dX partials stored in bf16 and their reduce, from trn's dU (timed after the pass).
+    half = pl.MLPTrainShard(blk.X, blk.W1, blk.W2, dZ, cfg.world, bf16_dx_partials=True)
+    half.dU = trn.dU
     legs = {"dY": lambda r: trn.backward_row(r, True, False),
             "dW2": lambda r: trn.backward_row(r, False, True),
             "dX_part": lambda r: trn.backward_col(r, True, False),
             "dW1": lambda r: trn.backward_col(r, False, True)}
-    ev = {k: [] for k in list(legs) + ["reduce_dX", "pass"]}
+    ev = {k: [] for k in list(legs) + ["reduce_dX", "pass", "dX_part_bf16", "reduce_dX_bf16"]}
     # Each product runs for all ranks back to back (rank r's dX and dW1 read its dU_r, which
     # its dY product wrote in an earlier group), with events only at the group boundaries.
     for it in range(3):
@@ -273,6 +277,19 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
         if it > 0:
             ev["reduce_dX"].append((prev, e_))
             ev["pass"].append((s0, e_))
+        prev = e_
+        for r in range(cfg.world):
+            half.backward_col(r, True, False)
+        e_ = torch.cuda.Event(enable_timing=True)
+        e_.record(stream)
+        if it > 0:
+            ev["dX_part_bf16"].append((prev, e_))
+        prev = e_
+        half.reduce_dx()
+        e_ = torch.cuda.Event(enable_timing=True)
+        e_.record(stream)
+        if it > 0:
+            ev["reduce_dX_bf16"].append((prev, e_))
     torch.cuda.synchronize()
     T, H, fl = cfg.tokens, cfg.hidden, cfg.ffn // cfg.world
     gemm_flops = 2.0 * T * H * fl  # each of the four products
@@ -289,7 +306,18 @@ def mlp_backward_leg(cfg, t, blk, stream) -> dict:
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev["pass"]]))
     out["pass_ms"] = round(ms, 3)
     out["pass_tflops"] = round(cfg.world * 4 * gemm_flops / ms / 1e9, 1)
-    del trn
+    # the variant with the dX partials exchanged in bf16 (the fp32 pass above is the measure)
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev["dX_part_bf16"]])) / cfg.world
+    out["dX_part_bf16"] = {"avg_ms": round(ms, 4), "tflops": round(gemm_flops / ms / 1e9, 1)}
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev["reduce_dX_bf16"]]))
+    nbytes = reduce_bytes(T, H, cfg.world, "bf16", residual=False, h_out=True, y_out=False,
+                          parts_dtype="bf16")
+    out["reduce_dX_bf16"] = {"avg_ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                             "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    out["pass_bf16_dx_ms"] = round(out["pass_ms"] + cfg.world * (out["dX_part_bf16"]["avg_ms"]
+                                   - out["dX_part"]["avg_ms"]) + out["reduce_dX_bf16"]["avg_ms"]
+                                   - out["reduce_dX"]["avg_ms"], 3)
+    del trn, half
     return out
 
 

@@ -130,7 +130,7 @@ int tp_row_linear_fold(const void* X, int64_t ldx, const void* W, float* Zsum,
  * Zpart[t, n] is the fp32 sum of tp_row_linear_partial,
  * rounded once to bf16 (nearest, ties to even) and written as a dense bf16 [seq, N] block;
  * tp_partial_reduce_residual_ln_bf16 then reads half the bytes of the fp32 partials.  The
- * partials' rounding adds to the error of the reduced sum (relative to its partials, 2^-9 per
+ * partials' rounding adds to the error of the reduced sum (relative to its partials, 2^-8 per
  * partial), so this is a variant beside the fp32-partial path, not a replacement.  Inputs are
  * bf16 (no dtype argument); X, ldx, W, shard addressing and errors are those of
  * tp_row_linear_partial (TP_ERR_DTYPE does not occur). */
@@ -199,6 +199,18 @@ int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t
                            float* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
                            int64_t N, int rank, int world, int accumulate, int dtype,
                            void* stream);
+
+/* tp_col_linear_backward with the input-gradient partial exchanged in bf16, as the forward
+ * partials of tp_row_linear_partial_bf16 are (pwwt.cn section 5.2 counts the all-reduce's
+ * [S, H] operand at 2 bytes per element; section 6.3 names BF16 and the summation order as
+ * the sources of error between TP and one device).  dXpart bf16 [seq, H] dense receives the
+ * fp32 sum of tp_col_linear_backward's dXpart, rounded once to bf16 (nearest, ties to even);
+ * tp_partial_reduce_residual_ln_bf16 (gamma = NULL) then sums the ranks' partials.  dW, the
+ * other arguments and the errors are those of tp_col_linear_backward with dtype TP_BF16 (no
+ * dtype argument, so no TP_ERR_DTYPE). */
+int tp_col_linear_backward_bf16(const void* X, const void* W, const void* dU, int64_t ldu,
+                                void* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
+                                int64_t N, int rank, int world, int accumulate, void* stream);
 
 /* Workspace bytes tp_attn_head_shard needs for these sizes on the current device; 0 if the
  * sizes are invalid.  It queries the device's compute-unit count (the QKV projection's launch

@@ -369,10 +369,15 @@ int tp_row_linear_backward(const void* dZ, const void* W, const void* Y, int64_t
   return TP_OK;
 }
 
-int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t ldu,
-                           float* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
-                           int64_t N, int rank, int world, int accumulate, int dtype,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+// tp_col_linear_backward with the input-gradient partial stored in fp32 (EPI_PARTIAL_F32) or
+// in bf16 (EPI_STORE).
+int col_linear_backward(const void* X, const void* W, const void* dU, int64_t ldu,
+                        void* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
+                        int64_t N, int rank, int world, int accumulate, int dtype, int dx_epi,
+                        void* stream) {
   if (!X || !W || !dU || (!dXpart && !dW)) return TP_ERR_NULL;
   if (dtype != TP_BF16) return TP_ERR_DTYPE;
   if (int st = check_rank(rank, world)) return st;
@@ -406,7 +411,7 @@ int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t
     g.N = H;
     g.K = nl;
     g.layout = LAY_NT;
-    g.epi = EPI_PARTIAL_F32;
+    g.epi = dx_epi;
     if (launch_gemm_bf16(g, st) != hipSuccess) return TP_ERR_LAUNCH;
   }
   if (dW) {  // dW[h, j] (+)= sum_t X[t, h] dU[t, j]
@@ -428,6 +433,24 @@ int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t
     if (launch_gemm_bf16(g, st) != hipSuccess) return TP_ERR_LAUNCH;
   }
   return TP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int tp_col_linear_backward(const void* X, const void* W, const void* dU, int64_t ldu,
+                           float* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
+                           int64_t N, int rank, int world, int accumulate, int dtype,
+                           void* stream) {
+  return col_linear_backward(X, W, dU, ldu, dXpart, dW, ld_dw, seq, H, N, rank, world,
+                             accumulate, dtype, EPI_PARTIAL_F32, stream);
+}
+
+int tp_col_linear_backward_bf16(const void* X, const void* W, const void* dU, int64_t ldu,
+                                void* dXpart, float* dW, int64_t ld_dw, int64_t seq, int64_t H,
+                                int64_t N, int rank, int world, int accumulate, void* stream) {
+  return col_linear_backward(X, W, dU, ldu, dXpart, dW, ld_dw, seq, H, N, rank, world,
+                             accumulate, TP_BF16, EPI_STORE, stream);
 }
 
 size_t tp_attn_workspace_bytes(int64_t batch, int64_t seq, int64_t H, int n_heads,

@@ -117,9 +117,12 @@ class MLPTrainShard:
     derivative fused in) and the rank's row block of dB; tp_col_linear_backward the rank's
     fp32 partial of dX and its column block of dA; reduce_dx sums the partials (the backward
     all-reduce) into dX (bf16).  dA [H, F] and dB [F, H] are fp32, each rank writing its own
-    block (the gradient is as sharded as the weight); accumulate=True adds to them."""
+    block (the gradient is as sharded as the weight); accumulate=True adds to them.
+    bf16_dx_partials=True stores the dX partials in bf16 (tp_col_linear_backward_bf16) and sums
+    them with tp_partial_reduce_residual_ln_bf16, halving the exchanged bytes."""
 
-    def __init__(self, X, A, B, dZ, world: int, accumulate: bool = False, stream=None):
+    def __init__(self, X, A, B, dZ, world: int, accumulate: bool = False, stream=None,
+                 bf16_dx_partials: bool = False):
         self.X, self.A, self.B, self.dZ = X, A, B, dZ
         self.T, self.H = X.shape
         self.F = A.shape[1]
@@ -133,7 +136,9 @@ class MLPTrainShard:
         self.Y = torch.empty_like(self.U)
         self.dU = torch.empty_like(self.U)
         self.parts = torch.empty(world, self.T, self.H, dtype=torch.float32, device=dev)
-        self.dXparts = torch.empty_like(self.parts)
+        self.bf16_dx_partials = bf16_dx_partials
+        self.dXparts = torch.empty(world, self.T, self.H, device=dev,
+                                   dtype=bf if bf16_dx_partials else torch.float32)
         self.dA = torch.zeros(self.H, self.F, dtype=torch.float32, device=dev)
         self.dB = torch.zeros(self.F, self.H, dtype=torch.float32, device=dev)
         self.Z = torch.empty(self.T, self.H, dtype=torch.float32, device=dev)
@@ -157,16 +162,26 @@ class MLPTrainShard:
                                   int(self.accumulate), tp.TP_BF16, self.stream)
 
     def backward_col(self, r: int, input_grad: bool = True, weight_grad: bool = True):
-        tp.tp_col_linear_backward(self.X, self.A, self.dU[r], self.fl,
-                                  self.dXparts[r] if input_grad else None,
-                                  self.dA[:, r * self.fl:] if weight_grad else None, self.F,
-                                  self.T, self.H, self.F, r, self.P, int(self.accumulate),
-                                  tp.TP_BF16, self.stream)
+        dXp = self.dXparts[r] if input_grad else None
+        dA = self.dA[:, r * self.fl:] if weight_grad else None
+        if self.bf16_dx_partials:
+            tp.tp_col_linear_backward_bf16(self.X, self.A, self.dU[r], self.fl, dXp, dA, self.F,
+                                           self.T, self.H, self.F, r, self.P,
+                                           int(self.accumulate), self.stream)
+        else:
+            tp.tp_col_linear_backward(self.X, self.A, self.dU[r], self.fl, dXp, dA, self.F,
+                                      self.T, self.H, self.F, r, self.P, int(self.accumulate),
+                                      tp.TP_BF16, self.stream)
 
     def reduce_dx(self):
-        tp.tp_partial_reduce_residual_ln(self.dXparts, self.P, self.T * self.H, None, None, None,
-                                         0.0, self.dX, None, self.T, self.H, tp.TP_BF16,
-                                         self.stream)
+        if self.bf16_dx_partials:
+            tp.tp_partial_reduce_residual_ln_bf16(self.dXparts, self.P, self.T * self.H, None,
+                                                  None, None, 0.0, self.dX, None, self.T,
+                                                  self.H, self.stream)
+        else:
+            tp.tp_partial_reduce_residual_ln(self.dXparts, self.P, self.T * self.H, None, None,
+                                             None, 0.0, self.dX, None, self.T, self.H,
+                                             tp.TP_BF16, self.stream)
 
     def forward(self):
         for r in range(self.P):

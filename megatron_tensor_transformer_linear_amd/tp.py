@@ -36,7 +36,8 @@ EXPORTED = ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_row_linear_fold",
             "tp_attn_head_shard_noalloc", "tp_partial_reduce_residual_ln",
             "tp_partial_reduce_scatter_residual_ln", "tp_row_linear_partial_bf16",
             "tp_attn_head_shard_bf16", "tp_partial_reduce_residual_ln_bf16",
-            "tp_partial_reduce_scatter_residual_ln_bf16", "tp_status_string")
+            "tp_partial_reduce_scatter_residual_ln_bf16", "tp_col_linear_backward_bf16",
+            "tp_status_string")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -61,6 +62,9 @@ lib.tp_row_linear_backward.restype = _int
 lib.tp_col_linear_backward.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
                                        _int, _int, _int, _int, _vp]
 lib.tp_col_linear_backward.restype = _int
+lib.tp_col_linear_backward_bf16.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64,
+                                            _i64, _int, _int, _int, _vp]
+lib.tp_col_linear_backward_bf16.restype = _int
 lib.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _int, _int, _int, _int]
 lib.tp_attn_workspace_bytes.restype = _sz
 lib.tp_attn_head_shard.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _int,
@@ -169,6 +173,15 @@ def tp_col_linear_backward(X, W, dU, ldu: int, dXpart, dW, ld_dw: int, seq: int,
                                              _ptr(dW), ld_dw, seq, H, N, rank, world,
                                              int(accumulate), dtype, _stream(stream)),
                   "tp_col_linear_backward")
+
+
+def tp_col_linear_backward_bf16(X, W, dU, ldu: int, dXpart, dW, ld_dw: int, seq: int, H: int,
+                                N: int, rank: int, world: int, accumulate: int,
+                                stream=None) -> int:
+    return _check(lib.tp_col_linear_backward_bf16(_ptr(X), _ptr(W), _ptr(dU), ldu, _ptr(dXpart),
+                                                  _ptr(dW), ld_dw, seq, H, N, rank, world,
+                                                  int(accumulate), _stream(stream)),
+                  "tp_col_linear_backward_bf16")
 
 
 def tp_attn_workspace_bytes(batch: int, seq: int, H: int, n_heads: int, head_dim: int, world: int,

@@ -59,6 +59,8 @@ int main() {
   expect("row bf16 valid -> launch", tp_row_linear_partial_bf16(P, 1024, P, P, 64, 1024, 256, 1, 2, nullptr), TP_ERR_LAUNCH);
   expect("attn bf16 valid -> launch", tp_attn_head_shard_bf16(P, P, P, P, 2, 128, 1024, 8, 128, 0, 2, 1, P, ws, nullptr), TP_ERR_LAUNCH);
   expect("reduce bf16 stride % 8", tp_partial_reduce_residual_ln_bf16(P, 2, 64 * 256 + 4, P, P, P, 1e-5f, P, P, 64, 256, nullptr), TP_ERR_ALIGN);
+  expect("col bwd bf16 valid -> launch", tp_col_linear_backward_bf16(P, P, P, 512, P, F, 512, 64, 256, 1024, 0, 2, 1, nullptr), TP_ERR_LAUNCH);
+  expect("col bwd bf16 misaligned dX", tp_col_linear_backward_bf16(P, P, P, 512, (char*)P + 8, F, 512, 64, 256, 1024, 0, 2, 1, nullptr), TP_ERR_ALIGN);
   expect("reduce bf16 valid -> launch", tp_partial_reduce_residual_ln_bf16(P, 2, 64 * 256, P, P, P, 1e-5f, P, P, 64, 256, nullptr), TP_ERR_LAUNCH);
   for (int s = 1; s >= -12; --s) {
     const char* str = tp_status_string(s);
@@ -83,6 +85,7 @@ int main() {
               valid_status("scatter", tp_partial_reduce_scatter_residual_ln(F, r + 1, c, P, P, P, 1e-5f, P, P, a, b, r, w, dt, nullptr));
             }
             valid_status("row bf16", tp_row_linear_partial_bf16(P, b, P, P, a, b, c, r, w, nullptr));
+            valid_status("col bwd bf16", tp_col_linear_backward_bf16(P, P, P, c, P, F, b, a, b, c, r, w, r & 1, nullptr));
             valid_status("reduce bf16", tp_partial_reduce_residual_ln_bf16(P, r + 1, c, P, P, P, 1e-5f, P, P, a, b, nullptr));
             valid_status("scatter bf16", tp_partial_reduce_scatter_residual_ln_bf16(P, r + 1, c, P, P, P, 1e-5f, P, P, a, b, r, w, nullptr));
           }

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for n in ("tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_head_shard",
               "tp_partial_reduce_residual_ln", "tp_attn_workspace_bytes", "tp_status_string",
               "tp_partial_reduce_scatter_residual_ln", "tp_col_linear_gelu_save",
-              "tp_row_linear_backward", "tp_col_linear_backward"):
+              "tp_row_linear_backward", "tp_col_linear_backward",
+              "tp_col_linear_backward_bf16"):
         assert n in names
 
 
@@ -183,6 +184,15 @@ def colb(tp, **kw):
     return tp.lib.tp_col_linear_backward(a["X"], a["W"], a["dU"], a["ldu"], a["dX"], a["dW"],
                                          a["ld_dw"], a["seq"], a["H"], a["N"], a["rank"],
                                          a["world"], a["acc"], a["dtype"], a["stream"])
+
+
+def colbh(tp, **kw):
+    a = dict(X=P, W=P, dU=P, ldu=512, dX=P, dW=P, ld_dw=512, seq=64, H=256, N=1024, rank=0,
+             world=2, acc=1, stream=None)
+    a.update(kw)
+    return tp.lib.tp_col_linear_backward_bf16(a["X"], a["W"], a["dU"], a["ldu"], a["dX"], a["dW"],
+                                              a["ld_dw"], a["seq"], a["H"], a["N"], a["rank"],
+                                              a["world"], a["acc"], a["stream"])
 
 
 def rowh(tp, **kw):
@@ -407,6 +417,15 @@ CASES = [
      "TP_ERR_SHAPE"),
     ("colb misaligned dX", colb, dict(dX=P + 8), "TP_ERR_ALIGN"),
     ("colb ldu % 8", colb, dict(ldu=516), "TP_ERR_ALIGN"),
+    # column-parallel linear backward, bf16 input-gradient partial
+    ("colb bf16 null W", colbh, dict(W=None), "TP_ERR_NULL"),
+    ("colb bf16 no output", colbh, dict(dX=None, dW=None), "TP_ERR_NULL"),
+    ("colb bf16 rank = world", colbh, dict(rank=2), "TP_ERR_RANK"),
+    ("colb bf16 seq 0", colbh, dict(seq=0), "TP_ERR_SHAPE"),
+    ("colb bf16 N % world", colbh, dict(world=3), "TP_ERR_DIVISIBLE"),
+    ("colb bf16 ld_dw < N/world", colbh, dict(ld_dw=504), "TP_ERR_SHAPE"),
+    ("colb bf16 misaligned dX", colbh, dict(dX=P + 8), "TP_ERR_ALIGN"),
+    ("colb bf16 H % 8", colbh, dict(H=252), "TP_ERR_ALIGN"),
 ]
 
 

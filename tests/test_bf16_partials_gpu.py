@@ -12,7 +12,7 @@ import torch
 
 import oracle.tp_oracle as O
 from gpu_helpers import check, check_exact, dev, dev_values, host, say
-from workloads import generate, get_config
+from workloads import generate, get_config, output_gradient
 from workloads.configs import small_variant
 from workloads.synth import integer_matrix
 
@@ -229,3 +229,115 @@ def test_full_block_bf16_partials(lib):
         for r in range(cfg.world):
             check(f"attention partial {r} (bf16)", sh.parts[r], ref["attn_parts"][r], "bf16")
     _check_block(sh, cfg, t, attn_checks, against_fp32=False)
+
+
+# ============================================================== backward: bf16 dX partials
+@pytest.mark.parametrize("seq,H,N,world", [(300, 264, 1088, 4), (72, 136, 528, 2)])
+def test_col_backward_bf16_integer_exact(lib, seq, H, N, world):
+    """Non-negative integer dU and W: every dX partial is an integer near N/world (above 256,
+    so most are rounded and many are ties), exact in fp32; the bf16 store must equal the
+    oracle's round_bf16 of the exact partial, and dW = X^T dU stays exact in fp32."""
+    tp, pl = lib
+    rng = np.random.Generator(np.random.PCG64(1400 + world))
+    X = integer_matrix(rng, (seq, H), -2, 2, "bf16")
+    W = integer_matrix(rng, (H, N), 0, 2, "bf16")
+    dU_full = integer_matrix(rng, (seq, N), 0, 2, "bf16")
+    nl = N // world
+    Xd, Wd, dUd = dev(X), dev(W), dev(dU_full)
+    parts = torch.full((world, seq, H), 9.0, dtype=torch.bfloat16, device="cuda:0")
+    dWfull = torch.full((H, N), 9.0, dtype=torch.float32, device="cuda:0")
+    for r in range(world):
+        say(f"  col backward bf16 dX integer seq={seq} H={H} N={N} world={world} rank={r}")
+        tp.tp_col_linear_backward_bf16(Xd, Wd, dUd[:, r * nl:], N, parts[r], dWfull[:, r * nl:],
+                                       N, seq, H, N, r, world, 0)
+    _sync()
+    ref = []
+    for r in range(world):
+        rdX, rdW = O.col_linear_backward_bf16(dU_full.values()[:, r * nl:(r + 1) * nl],
+                                              X.values(), W.values(), r, world)
+        check_exact(f"bf16 dX part rank {r}", parts[r], rdX, "bf16")
+        check_exact(f"dW block rank {r}", dWfull[:, r * nl:(r + 1) * nl], rdW, "f32")
+        ref.append(rdX)
+    assert any(np.any(np.abs(p) > 256) for p in ref), "no partial exercised the rounding"
+    dX = torch.empty(seq, H, dtype=torch.bfloat16, device="cuda:0")
+    tp.tp_partial_reduce_residual_ln_bf16(parts, world, seq * H, None, None, None, 0.0, dX, None,
+                                          seq, H)
+    _sync()
+    check_exact("dX (sum of bf16 partials)", dX, O.round_bf16(O.reduce_partials(ref)), "bf16")
+
+
+def test_col_backward_bf16_is_the_rounded_fp32_partial(lib):
+    """Random inputs through tp_col_linear_backward and tp_col_linear_backward_bf16: the bf16
+    dX partial is the fp32 one rounded to nearest even, element for element, and the weight
+    gradients are bit-identical."""
+    tp, pl = lib
+    seq, H, N, world, rank = 520, 392, 2048, 4, 2
+    rng = np.random.Generator(np.random.PCG64(1410))
+    nl = N // world
+    X, W, dU = rng.standard_normal((seq, H)), rng.standard_normal((H, N)), rng.standard_normal((seq, nl))
+    Xd, Wd, dUd = (dev_values(v, "bf16") for v in (X, W, dU))
+    dX32 = torch.empty(seq, H, dtype=torch.float32, device="cuda:0")
+    dX16 = torch.empty(seq, H, dtype=torch.bfloat16, device="cuda:0")
+    dW32 = torch.empty(H, nl, dtype=torch.float32, device="cuda:0")
+    dW16 = torch.empty_like(dW32)
+    say("  col backward fp32 / bf16 dX partial")
+    tp.tp_col_linear_backward(Xd, Wd, dUd, nl, dX32, dW32, nl, seq, H, N, rank, world, 0,
+                              tp.TP_BF16)
+    tp.tp_col_linear_backward_bf16(Xd, Wd, dUd, nl, dX16, dW16, nl, seq, H, N, rank, world, 0)
+    _sync()
+    check_exact("bf16 = rounded fp32", dX16, O.round_bf16(host(dX32)), "bf16")
+    assert torch.equal(dW32.view(torch.int32), dW16.view(torch.int32)), "dW differs"
+    rdX, rdW = O.col_linear_backward_bf16(host(dUd), host(Xd), host(Wd), rank, world)
+    check("bf16 dX partial", dX16, rdX, "bf16")
+
+
+@pytest.mark.parametrize("world", [2, 4])
+def test_small_mlp_backward_bf16_dx_partials(lib, world):
+    """The MLP backward with bf16 input-gradient partials against the oracle's mlp_backward
+    with rounded partials: every rank's partial, the reduced dX, and dA, dB."""
+    tp, pl = lib
+    cfg = small_variant("mlp_bf16_tp4").with_(world=world)
+    t = generate(cfg)
+    dZ = output_gradient(cfg)
+    sh = pl.MLPTrainShard(dev(t["X"]), dev(t["A"]), dev(t["B"]), dev(dZ), world,
+                          bf16_dx_partials=True)
+    say(f"  small MLP backward, bf16 dX partials, world={world}")
+    sh.forward()
+    sh.backward()
+    _sync()
+    X, A, B = t["X"].values(), t["A"].values(), t["B"].values()
+    ref = O.mlp_backward(X, A, B, dZ.values(), world, bf16_dx_partials=True)
+    for r in range(world):
+        s = O.mlp_shard_backward(X, A, B, dZ.values(), r, world, bf16_dx_partials=True)
+        check(f"bf16 dX part rank {r}", sh.dXparts[r], s["dX_part"], "bf16")
+    check("dX", sh.dX, ref["dX"], "bf16")
+    check("dA", sh.dA, ref["dA"], "bf16")
+    check("dB", sh.dB, ref["dB"], "bf16")
+    check("dX against fp32 partials", sh.dX, O.mlp_backward(X, A, B, dZ.values(), world)["dX"],
+          "bf16")
+
+
+@pytest.mark.timeout(300)
+def test_full_col_backward_bf16_is_the_rounded_fp32_partial(lib):
+    """The block workload's input-gradient product at full size (dU 8192 x 6144, W1 12288 x
+    49152, rank 5 of 8), in the launch the bench times: the bf16 partial is the fp32 partial
+    rounded to nearest even on every element."""
+    tp, pl = lib
+    cfg = get_config("block_bf16_tp8")
+    T, H, F, P = cfg.tokens, cfg.hidden, cfg.ffn, cfg.world
+    r, fl = 5, F // P
+    rng = np.random.Generator(np.random.PCG64(1420))
+    X = dev_values(rng.standard_normal((T, H), dtype=np.float32), "bf16")
+    W = torch.zeros(H, F, dtype=torch.bfloat16, device="cuda:0")   # only block r is read
+    W[:, r * fl:(r + 1) * fl] = dev_values(rng.standard_normal((H, fl), dtype=np.float32)
+                                           / np.sqrt(H), "bf16")
+    dU = dev_values(rng.standard_normal((T, fl), dtype=np.float32), "bf16")
+    dX32 = torch.empty(T, H, dtype=torch.float32, device="cuda:0")
+    dX16 = torch.empty(T, H, dtype=torch.bfloat16, device="cuda:0")
+    say(f"  full-size col backward fp32 / bf16 dX partial rank {r}")
+    tp.tp_col_linear_backward(X, W, dU, fl, dX32, None, F, T, H, F, r, P, 0, tp.TP_BF16)
+    tp.tp_col_linear_backward_bf16(X, W, dU, fl, dX16, None, F, T, H, F, r, P, 0)
+    _sync()
+    for i in range(0, T, 1024):
+        check_exact(f"rows {i}..{i + 1023}", dX16[i:i + 1024],
+                    O.round_bf16(host(dX32[i:i + 1024])), "bf16")
