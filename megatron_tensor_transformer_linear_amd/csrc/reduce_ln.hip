@@ -5,9 +5,14 @@
 //
 //   h = residual + sum_{p ascending} parts[p];  y = (h - mean) / sqrt(var + eps) * gamma + beta
 //
-// HBM-bound.  One workgroup per row at a time; each thread owns NCH runs of 8 consecutive elements
-// (32 bytes of every fp32 partial, 16 bytes of a bf16 row), spaced THREADS runs apart so a
-// wave's loads are contiguous.  The partials are read in two alternating register batches
+// HBM-bound.  One workgroup per row at a time; each thread owns NCH runs of 8 elements.  Over
+// fp32 partials with full rows, a run is two halves of 4 consecutive elements 256 apart (lane l
+// of wave w holds elements 4l.. and 256 + 4l.. of the wave's 512-element segment), so every
+// load and store instruction of a wave covers one contiguous range: 64 x 16 bytes of a
+// partial.  Eight consecutive elements per lane would leave each 16-byte load touching every
+// other 16 bytes of a 2 KB span, and a row sum of 8 fp32 partials over that layout measured 7 to
+// 10 % slower on MI355X.  Otherwise (bf16 partials, ragged rows) a run is 8 consecutive elements
+// (16 bytes of a bf16 row), runs spaced THREADS apart.  The partials are read in two alternating register batches
 // (partial p+1 in flight while p is added); then the residual row; then gamma and beta ahead
 // of the statistics.  The partials are read once and the outputs written once, so those
 // accesses are streaming (non-temporal): on MI355X that moves the fused reduce from 4.9 to
@@ -46,6 +51,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 // Cache policy of a buffer load: non-temporal (streaming; the partials are read once).
 constexpr int CPOL_NT = 2;
 
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
 // 8 consecutive elements of a bf16 or fp32 output row, written as streaming stores.
 template <bool BF16>
 __device__ __forceinline__ void store8(void* p, int64_t idx, const F8& r) {
@@ -83,6 +90,41 @@ __device__ __forceinline__ Raw8<BF16> load_raw8(const void* p, int64_t idx) {
   return r;
 }
 
+// A run of reduce_ln_kernel: elements idx .. idx+3 and idxb .. idxb+3 (idxb = idx + 4 unless
+// SPLIT), loaded into / stored from the 8 values in that order.
+template <bool BF16, bool SPLIT>
+__device__ __forceinline__ Raw8<BF16> load_run(const void* p, int64_t idx, int64_t idxb) {
+  if constexpr (BF16 && SPLIT) {
+    Raw8<BF16> r;
+    const uint2 a = *(const uint2*)((const bf16_t*)p + idx);
+    const uint2 b = *(const uint2*)((const bf16_t*)p + idxb);
+    r.u = make_uint4(a.x, a.y, b.x, b.y);
+    return r;
+  } else if constexpr (BF16) {
+    return load_raw8<true>(p, idx);
+  } else {
+    Raw8<BF16> r;
+    r.a = *(const f32x4_t*)((const float*)p + idx);
+    r.b = *(const f32x4_t*)((const float*)p + idxb);
+    return r;
+  }
+}
+
+template <bool BF16, bool SPLIT>
+__device__ __forceinline__ void store_run(void* p, int64_t idx, int64_t idxb, const F8& r) {
+  if constexpr (BF16 && SPLIT) {
+    __builtin_nontemporal_store(u32x2_t{pack_bf16x2(r.v[0], r.v[1]), pack_bf16x2(r.v[2], r.v[3])},
+                                (u32x2_t*)((bf16_t*)p + idx));
+    __builtin_nontemporal_store(u32x2_t{pack_bf16x2(r.v[4], r.v[5]), pack_bf16x2(r.v[6], r.v[7])},
+                                (u32x2_t*)((bf16_t*)p + idxb));
+  } else if constexpr (BF16) {
+    store8<true>(p, idx, r);
+  } else {
+    __builtin_nontemporal_store(f32x4_t{r.v[0], r.v[1], r.v[2], r.v[3]}, (f32x4_t*)((float*)p + idx));
+    __builtin_nontemporal_store(f32x4_t{r.v[4], r.v[5], r.v[6], r.v[7]}, (f32x4_t*)((float*)p + idxb));
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void unpack8(const Raw8<BF16>& r, float* v) {
   if constexpr (BF16) {
@@ -113,14 +155,23 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   __shared__ float red[THREADS / 64];
   const int tid = threadIdx.x;
   const int64_t H = r.H;
+  // SPLIT: each run is two 4-element halves, 256 elements apart (see the top of the file).
+  constexpr bool SPLIT = FULL && !PB;
   bool in[NCH];
-  int64_t col[NCH];
-  uint32_t boff[NCH];  // byte offset of the run in an fp32 row (past the row: out of range)
+  int64_t col[NCH], colb[NCH];  // first element of each half of the run
+  uint32_t boff[NCH], boffb[NCH];  // their byte offsets in an fp32 row (past the row: out of range)
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    col[c] = ((int64_t)c * THREADS + tid) * 8;
+    if constexpr (SPLIT) {
+      col[c] = ((int64_t)c * (THREADS / 64) + (tid >> 6)) * 512 + 4 * (tid & 63);
+      colb[c] = col[c] + 256;
+    } else {
+      col[c] = ((int64_t)c * THREADS + tid) * 8;
+      colb[c] = col[c] + 4;
+    }
     in[c] = FULL || col[c] < H;
     boff[c] = (uint32_t)col[c] * 4u;
+    boffb[c] = (uint32_t)colb[c] * 4u;
   }
   const int np = r.n_parts;
   // Partial p of row `row` into batch q: buffer loads from a resource spanning that row of the
@@ -139,7 +190,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
         q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] / 2, 0, CPOL_NT));
       } else {
         q[c][0] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c], 0, CPOL_NT));
-        q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boff[c] + 16, 0, CPOL_NT));
+        q[c][1] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, boffb[c], 0, CPOL_NT));
       }
     }
   };
@@ -155,8 +206,8 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
     for (int c = 0; c < NCH; ++c) {
       Raw8<BF16> g{}, b{};
       if (in[c]) {
-        g = load_raw8<BF16>(r.gamma, col[c]);
-        b = load_raw8<BF16>(beta, col[c]);
+        g = load_run<BF16, SPLIT>(r.gamma, col[c], colb[c]);
+        b = load_run<BF16, SPLIT>(beta, col[c], colb[c]);
       }
       gb_lds[0][c * THREADS + tid] = g;
       gb_lds[1][c * THREADS + tid] = b;
@@ -231,7 +282,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
     if constexpr (RES) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        if (in[c]) res[c] = load_raw8<BF16>(r.residual, roff + col[c]);
+        if (in[c]) res[c] = load_run<BF16, SPLIT>(r.residual, roff + col[c], roff + colb[c]);
     }
     Raw8<BF16> gm[NCH], bt[NCH];
     if constexpr (LN && !GB_LDS) {
@@ -239,8 +290,8 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         if (in[c]) {
-          gm[c] = load_raw8<BF16>(r.gamma, col[c]);
-          bt[c] = load_raw8<BF16>(beta, col[c]);
+          gm[c] = load_run<BF16, SPLIT>(r.gamma, col[c], colb[c]);
+          bt[c] = load_run<BF16, SPLIT>(beta, col[c], colb[c]);
         }
       }
     }
@@ -263,7 +314,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
           F8 o;
 #pragma unroll
           for (int e = 0; e < 8; ++e) o.v[e] = v[c][e];
-          store8<BF16>(r.h_out, ooff + col[c], o);
+          store_run<BF16, SPLIT>(r.h_out, ooff + col[c], ooff + colb[c], o);
         }
       }
 #pragma unroll
@@ -302,7 +353,7 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
         F8 y;
 #pragma unroll
         for (int e = 0; e < 8; ++e) y.v[e] = (v[c][e] - mean) * rstd * gv[e] + bv[e];
-        store8<BF16>(r.y_out, ooff + col[c], y);
+        store_run<BF16, SPLIT>(r.y_out, ooff + col[c], ooff + colb[c], y);
       }
     }
   }  // row loop
