@@ -639,6 +639,62 @@ def test_reduce_edge_cases(lib, dtype, rows, H, n_parts, residual, ln):
         check("y", yd, y, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H", [512, 1024, 2048, 4096, 6144, 8192, 12288, 16384, 24576, 32768])
+def test_reduce_every_full_width(lib, dtype, H):
+    """Rows that every thread's runs fill exactly, for each launch shape (64 to 1024 threads, 1
+    to 8 runs): over fp32 partials a run is two 4-element halves 256 apart, which every output
+    element must see the same as a ragged row would."""
+    tp, pl = lib
+    rows, n_parts = 37, 3
+    rng = np.random.Generator(np.random.PCG64(4100 + H))
+    parts = (rng.standard_normal((n_parts, rows, H)) * 2).astype(np.float32)
+    R = (rng.standard_normal((rows, H)) + 0.5).astype(np.float32)
+    g = (1 + 0.5 * rng.standard_normal(H)).astype(np.float32)
+    b = (0.5 * rng.standard_normal(H)).astype(np.float32)
+    Pd = torch.from_numpy(parts).to("cuda:0")
+    Rd, gd, bd = dev_values(R, dtype), dev_values(g, dtype), dev_values(b, dtype)
+    hd = torch.empty(rows, H, dtype=Rd.dtype, device="cuda:0")
+    yd = torch.empty_like(hd)
+    say(f"  reduce full width dtype={dtype} rows={rows} H={H} parts={n_parts}")
+    tp.tp_partial_reduce_residual_ln(Pd, n_parts, rows * H, Rd, gd, bd, 1e-5, hd, yd, rows, H,
+                                     tp.TP_BF16 if dtype == "bf16" else tp.TP_F32)
+    _sync()
+    h, y = O.reduce_residual_layernorm(list(parts), host(Rd), host(gd), host(bd), 1e-5)
+    check("h", hd, h, dtype)
+    check("y", yd, y, dtype)
+
+
+@pytest.mark.parametrize("H", [4096, 12288])
+def test_reduce_layouts_agree(lib, H):
+    """The same bf16-valued partials reduced as fp32 partials (two-half runs) and as bf16
+    partials (8 consecutive elements per run): each element's additions are the same, so h is
+    bit-identical; the LayerNorm statistics are summed in another lane order, so y may differ
+    by one bf16 step."""
+    tp, pl = lib
+    rows, n_parts = 129, 8
+    rng = np.random.Generator(np.random.PCG64(4200 + H))
+    P16 = dev_values(rng.standard_normal((n_parts, rows, H)), "bf16")
+    P32 = P16.float()
+    Rd = dev_values(rng.standard_normal((rows, H)), "bf16")
+    gd = dev_values(1 + 0.5 * rng.standard_normal(H), "bf16")
+    bd = dev_values(0.5 * rng.standard_normal(H), "bf16")
+    h32, y32, h16, y16 = (torch.empty(rows, H, dtype=torch.bfloat16, device="cuda:0")
+                          for _ in range(4))
+    say(f"  reduce layouts fp32 / bf16 partials rows={rows} H={H}")
+    tp.tp_partial_reduce_residual_ln(P32, n_parts, rows * H, Rd, gd, bd, 1e-5, h32, y32, rows, H,
+                                     tp.TP_BF16)
+    tp.tp_partial_reduce_residual_ln_bf16(P16, n_parts, rows * H, Rd, gd, bd, 1e-5, h16, y16,
+                                          rows, H)
+    _sync()
+    assert torch.equal(h32.view(torch.int16), h16.view(torch.int16)), "h differs"
+    # one bf16 step of |y| is at most 2^-7 |y|; near zero the fp32 statistics' own rounding
+    # (about 1e-6 of the row's scale) decides instead
+    a, b = y32.float(), y16.float()
+    excess = ((a - b).abs() - (2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 1e-5)).max()
+    assert float(excess) <= 0, f"y differs by more than one bf16 step ({float(excess)})"
+
+
 def test_errors_leave_outputs_untouched(lib):
     tp, pl = lib
     Xd = torch.ones(64, 256, dtype=torch.bfloat16, device="cuda:0")
