@@ -5,11 +5,11 @@
 //
 //   h = residual + sum_{p ascending} parts[p];  y = (h - mean) / sqrt(var + eps) * gamma + beta
 //
-// HBM-bound.  One workgroup per row at a time; each thread owns NCH runs of 8 elements.  Over
-// fp32 partials with full rows, a run is two halves of 4 consecutive elements 256 apart (lane l
-// of wave w holds elements 4l.. and 256 + 4l.. of the wave's 512-element segment), so every
-// load and store instruction of a wave covers one contiguous range: 64 x 16 bytes of a
-// partial.  Eight consecutive elements per lane would leave each 16-byte load touching every
+// HBM-bound.  One workgroup per row at a time; each thread owns NCH runs of 8 elements.  In a
+// full row (the runs fill it exactly) that is not summed from bf16 partials, a run is two
+// halves of 4 consecutive elements 256 apart (lane l of wave w holds elements 4l.. and
+// 256 + 4l.. of the wave's 512-element segment), so every load and store instruction of a
+// wave covers one contiguous range: 64 x 16 bytes of an fp32 partial.  Eight consecutive elements per lane would leave each 16-byte load touching every
 // other 16 bytes of a 2 KB span, and a row sum of 8 fp32 partials over that layout measured 7 to
 // 10 % slower on MI355X.  Otherwise (bf16 partials, ragged rows) a run is 8 consecutive elements
 // (16 bytes of a bf16 row), runs spaced THREADS apart.  The partials are read in two alternating register batches
@@ -155,7 +155,8 @@ __global__ __launch_bounds__(THREADS) void reduce_ln_kernel(ReduceDesc r) {
   __shared__ float red[THREADS / 64];
   const int tid = threadIdx.x;
   const int64_t H = r.H;
-  // SPLIT: each run is two 4-element halves, 256 elements apart (see the top of the file).
+  // SPLIT: each run is two 4-element halves, 256 elements apart (see the top of the file); a
+  // ragged row keeps 8 consecutive elements per run, so one bounds test covers the run.
   constexpr bool SPLIT = FULL && !PB;
   bool in[NCH];
   int64_t col[NCH], colb[NCH];  // first element of each half of the run
